@@ -1,0 +1,26 @@
+"""MI355X-native exact attention: FA-2 style forward, split-K decode and
+recomputation backward, as hand-written HIP kernels for gfx950 behind a
+C ABI (``libattn.so``, declared in ``include/attn.h``).
+
+The Python names mirror the C entry points; the shared library is loaded on
+first use, and every call fails loudly when it is missing.
+"""
+
+__all__ = [
+    "attn_fwd",
+    "attn_fwd_splitk_decode",
+    "attn_bwd",
+    "attn_decode_workspace_bytes",
+    "attn_bwd_workspace_bytes",
+    "attn_status_string",
+    "AttnError",
+    "library_path",
+]
+
+
+def __getattr__(name):
+    if name in __all__:
+        from . import binding
+
+        return getattr(binding, name)
+    raise AttributeError(name)

@@ -1,0 +1,274 @@
+"""fp64 NumPy reference of exact attention.  TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s cpu_baseline
+leg may use this module; the product path never does.
+
+Conventions shared by every function:
+
+* Tensors are NumPy arrays with any leading batch dimensions and the last two
+  dimensions [sequence, head_dim]; they are widened to float64 on entry, so a
+  bf16 or fp32 input is used at exactly the value the GPU reads.
+* ``scale`` multiplies Q K^T before the max and the exponential
+  ([xuesongtap] section 1; [Triton-ch8] section 8.1, where it is 1/sqrt(d)).
+* ``causal`` masks key position j > query position i with -inf
+  ([xuesongtap] section 2.2, last paragraph).  Query positions default to
+  0..Nq-1 (square, top-left aligned); ``q_pos`` overrides them so a subset of
+  query rows can be evaluated on its own.
+* LSE is the natural-log log-sum-exp of the scaled scores, m + ln(l)
+  ([xuesongtap] section 3; [Triton-ch8] section 8.8.2).
+* A row that sees no key at all (only possible through ``q_pos`` or an empty
+  key set) gets O = 0 and LSE = -inf; the pages leave this case open.
+"""
+
+import numpy as np
+
+NEG_INF = -np.inf
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def _visible(q_pos, k_pos, causal):
+    """Boolean [Nq, Nk]: True where query q_pos[i] may attend key k_pos[j]."""
+    if not causal:
+        return np.ones((len(q_pos), len(k_pos)), dtype=bool)
+    return k_pos[None, :] <= q_pos[:, None]
+
+
+def _scores(q, k, scale, causal, q_pos):
+    """S = scale * Q K^T with masked entries set to -inf ([xuesongtap] 1, 2.2)."""
+    S = scale * (q @ k.T)
+    vis = _visible(q_pos, np.arange(k.shape[0]), causal)
+    return np.where(vis, S, NEG_INF)
+
+
+def _softmax_rows(S):
+    """Numerically stable softmax per row ([Triton-ch8] section 8.3.1).
+
+    Returns (P, m, l): m is the row max, l = sum_j exp(S_ij - m_i) and
+    P = exp(S - m) / l.  Rows that are all -inf give P = 0, m = -inf, l = 0.
+    """
+    m = S.max(axis=1)
+    has_key = np.isfinite(m)
+    E = np.zeros_like(S)
+    E[has_key] = np.exp(S[has_key] - m[has_key, None])
+    l = E.sum(axis=1)
+    P = np.zeros_like(S)
+    P[has_key] = E[has_key] / l[has_key, None]
+    return P, m, l
+
+
+def _heads(shape):
+    return list(np.ndindex(*shape[:-2]))
+
+
+def ref_probs(q, k, scale, causal=False, q_pos=None):
+    """The attention probability matrix P = softmax(scale Q K^T) per head."""
+    q, k = _f64(q), _f64(k)
+    Nq = q.shape[-2]
+    q_pos = np.arange(Nq) if q_pos is None else np.asarray(q_pos)
+    P = np.zeros(q.shape[:-1] + (k.shape[-2],))
+    for h in _heads(q.shape):
+        P[h], _, _ = _softmax_rows(_scores(q[h], k[h], scale, causal, q_pos))
+    return P
+
+
+def ref_fwd(q, k, v, scale, causal=False, q_pos=None):
+    """Naive three-step attention: S, then P = softmax(S), then O = P V.
+
+    Follows the definition in [xuesongtap] section 1 and the naive
+    implementation of [Triton-ch8] section 8.1, with the LSE of
+    [xuesongtap] section 3.  Returns (O [..., Nq, dv], LSE [..., Nq]).
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    Nq = q.shape[-2]
+    q_pos = np.arange(Nq) if q_pos is None else np.asarray(q_pos)
+    O = np.zeros(q.shape[:-1] + (v.shape[-1],))
+    LSE = np.full(q.shape[:-1], NEG_INF)
+    for h in _heads(q.shape):
+        P, m, l = _softmax_rows(_scores(q[h], k[h], scale, causal, q_pos))
+        O[h] = P @ v[h]
+        has_key = l > 0
+        LSE[h][has_key] = m[has_key] + np.log(l[has_key])
+    return O, LSE
+
+
+def ref_bwd(q, k, v, dO, scale, causal=False, q_pos=None):
+    """Gradients of O = softmax(scale Q K^T) V with respect to Q, K and V.
+
+    P is rebuilt from Q and K (never from a saved LSE).  The formulas are
+    those of [Triton-ch8] sections 8.8.1 and 8.8.3 and [operatorworld]
+    (backward by recomputation):
+
+        dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij,
+        dS = P * (dP - D),  dQ = scale dS K,  dK = scale dS^T Q.
+
+    The Greek letter multiplying dS K and dS^T Q on the tutorial page is the
+    softmax scale (its kernel multiplies dq and dk by sm_scale in 8.8.4).
+    Returns (dQ, dK, dV).
+    """
+    q, k, v, dO = _f64(q), _f64(k), _f64(v), _f64(dO)
+    Nq = q.shape[-2]
+    q_pos = np.arange(Nq) if q_pos is None else np.asarray(q_pos)
+    dQ, dK, dV = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for h in _heads(q.shape):
+        P, _, _ = _softmax_rows(_scores(q[h], k[h], scale, causal, q_pos))
+        dV[h] = P.T @ dO[h]
+        dP = dO[h] @ v[h].T
+        D = (P * dP).sum(axis=1)
+        dS = P * (dP - D[:, None])
+        dQ[h] = scale * (dS @ k[h])
+        dK[h] = scale * (dS.T @ q[h])
+    return dQ, dK, dV
+
+
+def online_softmax_step(m_old, l_old, U_old, S_blk, V_blk):
+    """One inner-loop update of the running state (m, l, U) for a key block.
+
+    [xuesongtap] section 2.2 / [operatorworld] / [Triton-ch8] section 8.3.3:
+
+        m_new = max(m_old, rowmax(S_blk))
+        alpha = exp(m_old - m_new)         (0 while m_old is still -inf)
+        P~    = exp(S_blk - m_new)
+        l_new = alpha * l_old + rowsum(P~)
+        U_new = alpha * U_old + P~ V_blk
+
+    A row whose entries so far are all -inf keeps m = -inf, l = 0, U = 0
+    (the invalid difference -inf - (-inf) is never formed).
+    Returns (m_new, l_new, U_new, alpha).
+    """
+    m_new = np.maximum(m_old, S_blk.max(axis=1))
+    alpha = np.zeros_like(m_old)
+    seen = np.isfinite(m_old)
+    alpha[seen] = np.exp(m_old[seen] - m_new[seen])
+    base = np.where(np.isfinite(m_new), m_new, 0.0)
+    P_blk = np.exp(S_blk - base[:, None])
+    l_new = alpha * l_old + P_blk.sum(axis=1)
+    U_new = alpha[:, None] * U_old + P_blk @ V_blk
+    return m_new, l_new, U_new, alpha
+
+
+def ref_blockwise_fwd(q, k, v, scale, causal, Br, Bc, trace=False):
+    """FA-2 loop order: outer loop over Br-row query blocks, inner loop over
+    Bc-row key/value blocks, unnormalised U divided by l once at the end
+    ([xuesongtap] sections 2.1-2.2; [cnblogs] section 1 pseudocode).
+
+    Returns (O, LSE) or, with ``trace``, (O, LSE, trace) where
+    trace[head][(i0, j0)] = (m, l, alpha) after the block at rows i0 and
+    keys j0.  It exists to pin the online algebra; ref_fwd is the authority.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    Nq, Nk = q.shape[-2], k.shape[-2]
+    O = np.zeros(q.shape[:-1] + (v.shape[-1],))
+    LSE = np.full(q.shape[:-1], NEG_INF)
+    traces = {}
+    for h in _heads(q.shape):
+        tr = {}
+        for i0 in range(0, Nq, Br):
+            rows = np.arange(i0, min(i0 + Br, Nq))
+            Qi = q[h][rows]
+            m = np.full(len(rows), NEG_INF)
+            l = np.zeros(len(rows))
+            U = np.zeros((len(rows), v.shape[-1]))
+            for j0 in range(0, Nk, Bc):
+                cols = np.arange(j0, min(j0 + Bc, Nk))
+                S = scale * (Qi @ k[h][cols].T)
+                if causal:
+                    S = np.where(cols[None, :] <= rows[:, None], S, NEG_INF)
+                m, l, U, alpha = online_softmax_step(m, l, U, S, v[h][cols])
+                if trace:
+                    tr[(i0, j0)] = (m.copy(), l.copy(), alpha.copy())
+            has_key = l > 0
+            O[h][rows[has_key]] = U[has_key] / l[has_key, None]
+            LSE[h][rows[has_key]] = m[has_key] + np.log(l[has_key])
+        traces[h] = tr
+    if trace:
+        return O, LSE, traces
+    return O, LSE
+
+
+def decode_chunk_bounds(L, num_splits):
+    """Chunk c of a length-L cache covers keys [floor(cL/S), floor((c+1)L/S)).
+
+    The pages split the cache into blocks without fixing the rule for
+    L % S != 0; with S > L some chunks are empty.
+    """
+    return [((c * L) // num_splits, ((c + 1) * L) // num_splits) for c in range(num_splits)]
+
+
+def ref_decode_partials(q, k, v, scale, num_splits):
+    """Map step of FlashDecoding ([cnblogs] section 3 scenario B, step 2):
+    for each chunk c of the cache, the unnormalised partial state
+    ([FA1-vs-FA2] section 6)
+
+        m_c = max_j s_j,  l_c = sum_j exp(s_j - m_c),
+        U_c = sum_j exp(s_j - m_c) V_j,      s = scale K_c q.
+
+    q: [..., 1, d]; k, v: [..., L, d].  Returns (U [..., S, dv], m [..., S],
+    l [..., S]); an empty chunk gives U = 0, m = -inf, l = 0.
+    """
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    L = k.shape[-2]
+    bounds = decode_chunk_bounds(L, num_splits)
+    lead = q.shape[:-2]
+    U = np.zeros(lead + (num_splits, v.shape[-1]))
+    m = np.full(lead + (num_splits,), NEG_INF)
+    l = np.zeros(lead + (num_splits,))
+    for h in np.ndindex(*lead):
+        qv = q[h][0]
+        for c, (lo, hi) in enumerate(bounds):
+            if hi == lo:
+                continue
+            s = scale * (k[h][lo:hi] @ qv)
+            m[h][c] = s.max()
+            p = np.exp(s - m[h][c])
+            l[h][c] = p.sum()
+            U[h][c] = p @ v[h][lo:hi]
+    return U, m, l
+
+
+def merge_two(a, b):
+    """Merge two partial states (U, m, l) into one ([FA1-vs-FA2] section 6):
+    m = max(m_a, m_b), l = sum_w e^(m_w - m) l_w, U = sum_w e^(m_w - m) U_w.
+    A state with m = -inf (an empty chunk) has weight 0."""
+    Ua, ma, la = a
+    Ub, mb, lb = b
+    m = max(ma, mb)
+    if m == NEG_INF:
+        return np.zeros_like(Ua), NEG_INF, 0.0
+    wa = 0.0 if ma == NEG_INF else np.exp(ma - m)
+    wb = 0.0 if mb == NEG_INF else np.exp(mb - m)
+    return wa * Ua + wb * Ub, m, wa * la + wb * lb
+
+
+def merge_partials_tree(U, m, l):
+    """Reduce step of FlashDecoding: merge the per-chunk states pairwise in a
+    tree ([cnblogs] section 3 scenario B, step 3), then O = U / l and
+    LSE = m + ln l.  U: [S, dv]; m, l: [S].  Returns (O [dv], LSE)."""
+    states = [(U[c], m[c], l[c]) for c in range(len(m))]
+    while len(states) > 1:
+        nxt = [merge_two(states[i], states[i + 1]) for i in range(0, len(states) - 1, 2)]
+        if len(states) % 2:
+            nxt.append(states[-1])
+        states = nxt
+    Uf, mf, lf = states[0]
+    if lf == 0:
+        return np.zeros_like(Uf), NEG_INF
+    return Uf / lf, mf + np.log(lf)
+
+
+def ref_splitk_decode(q, k, v, scale, num_splits):
+    """Split-K decode: per-chunk partials, then the pairwise merge.
+
+    q: [..., 1, d]; k, v: [..., L, d].  Returns (O [..., 1, dv],
+    LSE [..., 1]).  The definition it must equal is ref_fwd with one query
+    row that sees every key.
+    """
+    U, m, l = ref_decode_partials(q, k, v, scale, num_splits)
+    lead = U.shape[:-2]
+    O = np.zeros(lead + (1, U.shape[-1]))
+    LSE = np.full(lead + (1,), NEG_INF)
+    for h in np.ndindex(*lead):
+        O[h][0], LSE[h][0] = merge_partials_tree(U[h], m[h], l[h])
+    return O, LSE

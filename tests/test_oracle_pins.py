@@ -1,0 +1,434 @@
+"""Pins of the fp64 oracle against values and properties the pages and the
+mathematics fix.  CPU only.
+
+Each pin is chosen so that a plausible mistake in the oracle (a missing
+rescale, a dropped term, a wrong sign, a transposed operand, a wrong scale
+placement) fails at least one of them; the mutation tests at the bottom plant
+such mistakes and check that they are caught.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from oracle import attention_ref as ar
+from exact_attention_05_amd.inputs import worked_example_qkv
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ---------------------------------------------------------------------------
+# The 4-token worked example ([cnblogs] section 2)
+# ---------------------------------------------------------------------------
+
+def _worked_inputs(d=4):
+    q, k, v = worked_example_qkv(d, torch.float32)
+    return q.double().numpy(), k.double().numpy(), v.double().numpy()
+
+
+def test_worked_example_scores_match_page():
+    g = _golden("worked_example.json")
+    q, k, _ = _worked_inputs()
+    S = q[0, 0] @ k[0, 0].T
+    assert np.array_equal(S[:2, :2], np.array(g["S11"], float))
+    assert np.array_equal(S[:2, 2:], np.array(g["S12"], float))
+
+
+def test_worked_example_blockwise_trace_matches_page():
+    g = _golden("worked_example.json")
+    q, k, v = _worked_inputs()
+    B = g["block"]
+    _, _, tr = ar.ref_blockwise_fwd(q, k, v, 1.0, False, B, B, trace=True)
+    tr = tr[(0, 0)]
+    m1, l1, a1 = tr[(0, 0)]
+    m2, l2, a2 = tr[(0, 2)]
+    assert np.array_equal(m1, np.array(g["m_after_block1"], float))
+    # first non-empty block: the old contribution's coefficient is 0
+    assert np.array_equal(a1, np.zeros(2))
+    # after block 2 the running max is the max of the old max and the block max
+    assert np.array_equal(m2, np.maximum(m1, np.array(g["blockmax_block2"], float)))
+    # row 0 is rescaled by e^(20-30); row 1's max does not grow, so its factor is exactly 1
+    assert a2[0] == pytest.approx(math.exp(g["row0_rescale_exponent"]), rel=1e-15)
+    assert a2[1] == 1.0
+
+
+def test_worked_example_closed_form():
+    """Final probabilities by hand: row 0 scores [10, 20, 30, 5], row 1 [10, 10, 5, 5]."""
+    q, k, v = _worked_inputs()
+    O, LSE = ar.ref_fwd(q, k, v, 1.0, False)
+    e5, e10, e20, e25 = (math.exp(-x) for x in (5, 10, 20, 25))
+    z0 = 1.0 + e10 + e20 + e25  # factor out e^30
+    row0 = np.array([e20, e10, 1.0, e25]) / z0
+    lse0 = 30.0 + math.log(z0)
+    z1 = 2.0 * (1.0 + e5)  # factor out e^10
+    row1 = np.array([1.0, 1.0, e5, e5]) / z1
+    lse1 = 10.0 + math.log(z1)
+    for r in range(4):  # V = I, so O rows are the probability rows; rows 2, 3 repeat 0, 1
+        want, wl = (row0, lse0) if r % 2 == 0 else (row1, lse1)
+        np.testing.assert_allclose(O[0, 0, r], want, rtol=1e-13, atol=1e-300)
+        assert LSE[0, 0, r] == pytest.approx(wl, rel=1e-15)
+
+
+def test_worked_example_online_equals_one_shot():
+    """[cnblogs] section 2 note: the online merge equals a one-shot softmax."""
+    q, k, v = _worked_inputs()
+    O1, L1 = ar.ref_fwd(q, k, v, 1.0, False)
+    for Br in (1, 2, 4):
+        for Bc in (1, 2, 3, 4):
+            O2, L2 = ar.ref_blockwise_fwd(q, k, v, 1.0, False, Br, Bc)
+            np.testing.assert_allclose(O2, O1, rtol=1e-13, atol=1e-300)
+            np.testing.assert_allclose(L2, L1, rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# alpha pins ([Triton-ch8] exercise; [operatorworld] degeneration checks)
+# ---------------------------------------------------------------------------
+
+def test_alpha_exercise_value():
+    g = _golden("alpha_exercise.json")
+    n_before = g["blocks_before_jump"]
+    Bc = 3
+    # one query row; a key block's score max is set through q . k_j with q = e_0
+    N = (n_before + 1) * Bc
+    q = np.zeros((1, 1, 1, 2))
+    q[..., 0] = 1.0
+    k = np.zeros((1, 1, N, 2))
+    k[0, 0, :, 0] = -5.0
+    for b in range(n_before):
+        k[0, 0, b * Bc, 0] = g["m_old"]
+    k[0, 0, n_before * Bc + 1, 0] = g["m_new"]
+    v = _rand((1, 1, N, 2), 0)
+    _, _, tr = ar.ref_blockwise_fwd(q, k, v, 1.0, False, 1, Bc, trace=True)
+    tr = tr[(0, 0)]
+    for b in range(1, n_before):
+        m, _, a = tr[(0, b * Bc)]
+        assert m[0] == g["m_old"] and a[0] == 1.0  # max unchanged: factor exactly 1
+    m, _, a = tr[(0, n_before * Bc)]
+    assert m[0] == g["m_new"]
+    assert a[0] == pytest.approx(g["alpha"], rel=1e-14)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_single_block_degenerates_to_softmax(causal):
+    q, k, v = (_rand((2, 3, 7, 5), s) for s in (1, 2, 3))
+    O1, L1 = ar.ref_fwd(q, k, v, 0.4, causal)
+    O2, L2, tr = ar.ref_blockwise_fwd(q, k, v, 0.4, causal, 7, 7, trace=True)
+    np.testing.assert_allclose(O2, O1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(L2, L1, rtol=1e-12)
+    for h in tr:
+        (_, _, a), = tr[h].values()
+        assert np.all(a == 0.0)
+
+
+# ---------------------------------------------------------------------------
+# Closed forms and invariants
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_rows_sum_to_one(causal):
+    q, k = _rand((2, 2, 9, 6), 4), _rand((2, 2, 9, 6), 5)
+    v = np.ones((2, 2, 9, 3))
+    O, LSE = ar.ref_fwd(q, k, v, 0.7, causal)
+    assert np.max(np.abs(O - 1.0)) <= 1e-14
+    S = 0.7 * np.einsum("bhid,bhjd->bhij", q, k)
+    if causal:
+        S = np.where(np.tril(np.ones((9, 9), bool)), S, -np.inf)
+    np.testing.assert_allclose(np.exp(S - LSE[..., None]).sum(-1), 1.0, rtol=1e-14)
+
+
+def test_uniform_scores_noncausal():
+    N = 11
+    q = np.zeros((1, 2, N, 4))
+    k, v = _rand((1, 2, N, 4), 6), _rand((1, 2, N, 5), 7)
+    O, LSE = ar.ref_fwd(q, k, v, 0.5, False)
+    np.testing.assert_allclose(O, np.broadcast_to(v.mean(axis=2, keepdims=True), O.shape), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(LSE, math.log(N), rtol=1e-15)
+
+
+def test_uniform_scores_causal():
+    N = 10
+    k = np.zeros((1, 1, N, 4))
+    q, v = _rand((1, 1, N, 4), 8), _rand((1, 1, N, 3), 9)
+    O, LSE = ar.ref_fwd(q, k, v, 1.3, True)
+    for i in range(N):
+        np.testing.assert_allclose(O[0, 0, i], v[0, 0, : i + 1].mean(axis=0), rtol=1e-13, atol=1e-15)
+        assert LSE[0, 0, i] == pytest.approx(math.log(i + 1), abs=1e-15)
+
+
+def test_uniform_scores_causal_backward():
+    N = 8
+    k = np.zeros((1, 1, N, 3))
+    q, v, dO = (_rand((1, 1, N, 3), s) for s in (10, 11, 12))
+    _, _, dV = ar.ref_bwd(q, k, v, dO, 0.9, True)
+    for j in range(N):
+        want = sum(dO[0, 0, i] / (i + 1) for i in range(j, N))
+        np.testing.assert_allclose(dV[0, 0, j], want, rtol=1e-13, atol=1e-15)
+    q0 = np.zeros_like(q)
+    _, dK, _ = ar.ref_bwd(q0, _rand((1, 1, N, 3), 13), v, dO, 0.9, True)
+    assert np.all(dK == 0.0)  # dK = scale dS^T Q vanishes with Q = 0
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_shift_invariance(causal):
+    q, k, v = (_rand((1, 2, 8, 4), s) for s in (14, 15, 16))
+    c = _rand((4,), 17)
+    O1, L1 = ar.ref_fwd(q, k, v, 0.6, causal)
+    O2, L2 = ar.ref_fwd(q, k + c, v, 0.6, causal)
+    np.testing.assert_allclose(O2, O1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(L2, L1 + 0.6 * (q @ c), rtol=1e-12, atol=1e-13)
+
+
+def test_q_pos_subset_matches_full_rows():
+    q, k, v = (_rand((1, 1, 12, 4), s) for s in (18, 19, 20))
+    O, LSE = ar.ref_fwd(q, k, v, 0.5, True)
+    rows = np.array([0, 5, 11])
+    O2, L2 = ar.ref_fwd(q[:, :, rows], k, v, 0.5, True, q_pos=rows)
+    np.testing.assert_allclose(O2, O[:, :, rows], rtol=1e-14)
+    np.testing.assert_allclose(L2, LSE[:, :, rows], rtol=1e-14)
+
+
+def test_fully_masked_row_reading():
+    """A query that sees no key (reachable only through q_pos) gives O = 0, LSE = -inf."""
+    q, k, v = (_rand((1, 1, 4, 3), s) for s in (21, 22, 23))
+    O, LSE = ar.ref_fwd(q[:, :, :1], k[:, :, 2:], v[:, :, 2:], 1.0, True, q_pos=np.array([-1]))
+    assert np.all(O == 0.0) and LSE[0, 0, 0] == -np.inf
+
+
+# ---------------------------------------------------------------------------
+# Brute force: blockwise online == global, every block shape on tiny N
+# ---------------------------------------------------------------------------
+
+@settings(max_examples=150, deadline=None)
+@given(
+    N=st.integers(1, 16),
+    br=st.integers(1, 16),
+    bc=st.integers(1, 16),
+    causal=st.booleans(),
+    seed=st.integers(0, 10_000),
+)
+def test_blockwise_equals_global(N, br, bc, causal, seed):
+    Br, Bc = min(br, N), min(bc, N)
+    rng = np.random.default_rng(seed)
+    q, k = rng.standard_normal((1, 1, N, 3)) * 3, rng.standard_normal((1, 1, N, 3)) * 3
+    v = rng.standard_normal((1, 1, N, 2))
+    O1, L1 = ar.ref_fwd(q, k, v, 0.8, causal)
+    O2, L2 = ar.ref_blockwise_fwd(q, k, v, 0.8, causal, Br, Bc)
+    np.testing.assert_allclose(O2, O1, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(L2, L1, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Independent implementations: scipy's softmax/logsumexp, torch SDPA in fp64
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_against_scipy(causal):
+    from scipy.special import logsumexp, softmax
+
+    q, k, v = (_rand((2, 2, 13, 8), s) for s in (24, 25, 26))
+    O, LSE = ar.ref_fwd(q, k, v, 0.35, causal)
+    S = 0.35 * np.einsum("bhid,bhjd->bhij", q, k)
+    if causal:
+        S = np.where(np.tril(np.ones((13, 13), bool)), S, -np.inf)
+    np.testing.assert_allclose(O, softmax(S, axis=-1) @ v, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(LSE, logsumexp(S, axis=-1), rtol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_forward_backward_against_torch_autograd(causal):
+    import torch.nn.functional as F
+
+    q, k, v, dO = (_rand((2, 3, 10, 6), s) for s in (27, 28, 29, 30))
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    out = F.scaled_dot_product_attention(tq, tk, tv, is_causal=causal, scale=0.45)
+    out.backward(torch.tensor(dO))
+    O, _ = ar.ref_fwd(q, k, v, 0.45, causal)
+    dQ, dK, dV = ar.ref_bwd(q, k, v, dO, 0.45, causal)
+    np.testing.assert_allclose(O, out.detach().numpy(), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(dQ, tq.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dK, tk.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dV, tv.grad.numpy(), rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Backward: central finite differences, and the rowsum invariants
+# ---------------------------------------------------------------------------
+
+def _loss(q, k, v, dO, scale, causal):
+    O, _ = ar.ref_fwd(q, k, v, scale, causal)
+    return float((O * dO).sum())
+
+
+def _fd_grad(x, f, h=1e-6):
+    g = np.zeros_like(x)
+    for idx in np.ndindex(*x.shape):
+        xp, xm = x.copy(), x.copy()
+        xp[idx] += h
+        xm[idx] -= h
+        g[idx] = (f(xp) - f(xm)) / (2 * h)
+    return g
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,d", [(1, 2), (5, 3), (6, 4)])
+def test_backward_finite_differences(causal, N, d):
+    q, k, v, dO = (_rand((1, 1, N, d), s) for s in (31, 32, 33, 34))
+    s = 0.7
+    dQ, dK, dV = ar.ref_bwd(q, k, v, dO, s, causal)
+    gq = _fd_grad(q, lambda x: _loss(x, k, v, dO, s, causal))
+    gk = _fd_grad(k, lambda x: _loss(q, x, v, dO, s, causal))
+    gv = _fd_grad(v, lambda x: _loss(q, k, x, dO, s, causal))
+    for got, want in ((dQ, gq), (dK, gk), (dV, gv)):
+        np.testing.assert_allclose(got, want, rtol=1e-6, atol=1e-8)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_invariants(causal):
+    q, k, v, dO = (_rand((1, 2, 9, 5), s) for s in (35, 36, 37, 38))
+    _, dK, _ = ar.ref_bwd(q, k, v, dO, 0.5, causal)
+    # rowsum_j dS_ij = 0 for every i, hence sum_j dK_j = scale sum_i (sum_j dS_ij) Q_i = 0
+    np.testing.assert_allclose(dK.sum(axis=2), 0.0, atol=1e-13)
+    # D_i = rowsum(P o dP) equals dO_i . O_i
+    P = ar.ref_probs(q, k, 0.5, causal)
+    O, _ = ar.ref_fwd(q, k, v, 0.5, causal)
+    dP = dO @ np.swapaxes(v, -1, -2)
+    np.testing.assert_allclose((P * dP).sum(-1), (dO * O).sum(-1), rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Split-K decode
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("S", [1, 2, 3, 7, 64, 97, 102])
+def test_splitk_decode_equals_definition(S):
+    L = 97
+    q = _rand((2, 2, 1, 6), 39)
+    k, v = _rand((2, 2, L, 6), 40), _rand((2, 2, L, 6), 41)
+    O1, L1 = ar.ref_fwd(q, k, v, 0.4, False)
+    O2, L2 = ar.ref_splitk_decode(q, k, v, 0.4, S)
+    np.testing.assert_allclose(O2, O1, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(L2, L1, rtol=1e-13)
+
+
+def test_decode_chunk_bounds_cover_cache():
+    for L, S in ((97, 7), (5, 8), (32768, 256), (1, 1)):
+        b = ar.decode_chunk_bounds(L, S)
+        assert b[0][0] == 0 and b[-1][1] == L
+        assert all(b[i][1] == b[i + 1][0] for i in range(S - 1))
+        assert all(hi - lo in (L // S, L // S + 1) for lo, hi in b)
+
+
+def test_decode_partials_single_chunk_is_plain_softmax_state():
+    """With one chunk the partial state is (sum e^(s-m) V, max s, sum e^(s-m))."""
+    from scipy.special import logsumexp
+
+    q, k, v = _rand((1, 1, 1, 4), 42), _rand((1, 1, 9, 4), 43), _rand((1, 1, 9, 4), 44)
+    U, m, l = ar.ref_decode_partials(q, k, v, 0.5, 1)
+    s = 0.5 * (k[0, 0] @ q[0, 0, 0])
+    assert m[0, 0, 0] == s.max()
+    assert m[0, 0, 0] + math.log(l[0, 0, 0]) == pytest.approx(logsumexp(s), rel=1e-15)
+
+
+def test_decode_uniform_and_ones():
+    L = 33
+    q = np.zeros((1, 1, 1, 4))
+    k, v = _rand((1, 1, L, 4), 45), _rand((1, 1, L, 4), 46)
+    O, LSE = ar.ref_splitk_decode(q, k, v, 1.0, 5)
+    np.testing.assert_allclose(O[0, 0, 0], v[0, 0].mean(axis=0), rtol=1e-13, atol=1e-15)
+    assert LSE[0, 0, 0] == pytest.approx(math.log(L), rel=1e-15)
+    O, _ = ar.ref_splitk_decode(_rand((1, 1, 1, 4), 47), k, np.ones((1, 1, L, 4)), 1.0, 40)
+    assert np.max(np.abs(O - 1.0)) <= 1e-14
+
+
+# ---------------------------------------------------------------------------
+# Mutation tests: plausible oracle mistakes must fail the pins above
+# ---------------------------------------------------------------------------
+
+_TRUE_STEP = ar.online_softmax_step
+
+
+def _no_rescale_step(m_old, l_old, U_old, S_blk, V_blk):
+    """The 'most common bug' of [operatorworld]: old U is not rescaled."""
+    m_new, l_new, _, alpha = _TRUE_STEP(m_old, l_old, U_old, S_blk, V_blk)
+    base = np.where(np.isfinite(m_new), m_new, 0.0)
+    U_new = U_old + np.exp(S_blk - base[:, None]) @ V_blk
+    return m_new, l_new, U_new, alpha
+
+
+def test_mutant_no_rescale_fails_worked_example(monkeypatch):
+    monkeypatch.setattr(ar, "online_softmax_step", _no_rescale_step)
+    q, k, v = _worked_inputs()
+    O_bad, _ = ar.ref_blockwise_fwd(q, k, v, 1.0, False, 2, 2)
+    O, _ = ar.ref_fwd(q, k, v, 1.0, False)
+    # row 0 weights key 1 at about e^-10 in truth, but at about 1 in the mutant
+    assert O_bad[0, 0, 0, 1] > 0.4 and O[0, 0, 0, 1] < 1e-4
+
+
+def _bwd_mutant(q, k, v, dO, scale, causal, kind):
+    P = ar.ref_probs(q, k, scale, causal)[0, 0]
+    q, k, v, dO = q[0, 0], k[0, 0], v[0, 0], dO[0, 0]
+    dV = P.T @ dO
+    dP = dO @ v.T
+    D = (P * dP).sum(axis=1)
+    if kind == "drop_D":
+        D = 0 * D
+    dS = P * (dP - D[:, None])
+    if kind == "sign":
+        dS = P * (D[:, None] - dP)
+    dQ = scale * (dS @ k)
+    dK = scale * (dS.T @ q)
+    if kind == "transpose":
+        dK = scale * (dS @ q)
+    if kind == "no_scale":
+        dQ = dS @ k
+    if kind == "dV_no_transpose":
+        dV = P @ dO
+    return dQ, dK, dV
+
+
+@pytest.mark.parametrize("kind", ["drop_D", "sign", "transpose", "no_scale", "dV_no_transpose"])
+def test_mutant_backward_fails_finite_differences(kind):
+    N, d, s = 5, 3, 0.7
+    q, k, v, dO = (_rand((1, 1, N, d), x) for x in (31, 32, 33, 34))
+    bad = _bwd_mutant(q, k, v, dO, s, True, kind)
+    good = ar.ref_bwd(q, k, v, dO, s, True)
+    gq = _fd_grad(q, lambda x: _loss(x, k, v, dO, s, True))
+    gk = _fd_grad(k, lambda x: _loss(q, x, v, dO, s, True))
+    gv = _fd_grad(v, lambda x: _loss(q, k, x, dO, s, True))
+    fd = (gq[0, 0], gk[0, 0], gv[0, 0])
+    err_bad = max(np.max(np.abs(b - f)) for b, f in zip(bad, fd))
+    err_good = max(np.max(np.abs(g[0, 0] - f)) for g, f in zip(good, fd))
+    assert err_good < 1e-7 and err_bad > 1e-3
+
+
+def test_mutant_merge_without_weights_fails_decode_pin(monkeypatch):
+    def bad_merge(a, b):
+        m = max(a[1], b[1])
+        return a[0] + b[0], m, a[2] + b[2]
+
+    monkeypatch.setattr(ar, "merge_two", bad_merge)
+    q = _rand((1, 1, 1, 6), 39)
+    k, v = _rand((1, 1, 50, 6), 40) * 2, _rand((1, 1, 50, 6), 41)
+    O1, _ = ar.ref_fwd(q, k, v, 1.0, False)
+    O2, _ = ar.ref_splitk_decode(q, k, v, 1.0, 4)
+    assert np.max(np.abs(O2 - O1)) > 1e-3
+
+
+def test_oracle_exports():
+    for name in oracle.__all__ if hasattr(oracle, "__all__") else ():
+        assert callable(getattr(oracle, name))
