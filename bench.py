@@ -1,0 +1,270 @@
+"""Benchmark of the attention hot path on one MI355X.
+
+One step = one pass of every kernel on the path over resident synthetic
+inputs:
+  * forward,  bf16 [B=4, H=16, N=2048, d=64], non-causal  (the headline)
+  * split-K decode, q bf16 [16, 32, 1, 128] against a K/V cache
+    [16, 32, 32768, 128] in 256 chunks (map + merge)
+  * backward, bf16 [2, 16, 4096, 64], causal (preprocess + dK/dV + dQ)
+  * forward, bf16 [2, 32, 8192, 128], causal, inputs x 0.5 (reported only)
+
+`value` is the forward's TFLOP/s (4*B*H*N^2*d per call) from HIP events
+around its launch on the launch stream, averaged over the timed steps.
+Prints one JSON line.
+"""
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz, dense
+PEAK_HBM_GBPS = 8000.0
+METRIC = "attn fwd TFLOP/s + % bf16 MFMA peak (B4 H16 N2048 d64); decode HBM GB/s"
+
+FWD = dict(B=4, H=16, N=2048, d=64, causal=False, input_scale=1.0)
+FWD_LONG = dict(B=2, H=32, N=8192, d=128, causal=True, input_scale=0.5)
+DEC = dict(B=16, H=32, L=32768, d=128, S=256)
+BWD = dict(B=2, H=16, N=4096, d=64, causal=True)
+
+
+def fwd_flops(c):
+    f = 4.0 * c["B"] * c["H"] * c["N"] ** 2 * c["d"]
+    return f / 2 if c["causal"] else f
+
+
+def fwd_bytes(c):
+    # Q, K, V read once, O written once (bf16), LSE written (fp32)
+    n = c["B"] * c["H"] * c["N"]
+    return 4 * n * c["d"] * 2 + n * 4
+
+
+def dec_bytes(c):
+    # K and V caches read once, q read and O written (bf16), LSE written (fp32)
+    bh = c["B"] * c["H"]
+    return 2 * bh * c["L"] * c["d"] * 2 + 2 * bh * c["d"] * 2 + bh * 4
+
+
+def _src_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "exact_attention_05_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _traffic(kernel_key, src_names, launches_bytes_unit=None):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is absent or was taken from another version of the kernel."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            tab = json.load(f)
+    except (OSError, ValueError):
+        return None
+    ent = tab.get(kernel_key)
+    if not ent or ent.get("source_sha") != _src_sha(*src_names):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+def cpu_baseline(budget_s=12.0):
+    """The fp64 oracle on a bounded sample of the forward workload (whole
+    heads of [4, 16, 2048, 64]), on this host's cores; TFLOP/s over the sample."""
+    import numpy as np
+    import torch
+
+    from exact_attention_05_amd.inputs import make_head, widen
+    from oracle import ref_fwd
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    c = FWD
+    scale = 1.0 / math.sqrt(c["d"])
+    heads = 0
+    t_total = 0.0
+    while heads < c["B"] * c["H"] and t_total < budget_s:
+        b, h = divmod(heads, c["H"])
+        q, k, v = (widen(make_head(0, n, b, h, c["N"], c["d"], torch.bfloat16)) for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        ref_fwd(q[None, None], k[None, None], v[None, None], scale, False)
+        t_total += time.perf_counter() - t0
+        heads += 1
+    flops = 4.0 * heads * c["N"] ** 2 * c["d"]
+    del np
+    return {
+        "value": round(flops / t_total / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(cores),
+        "kind": "oracle",
+        "sample": f"{heads} of {c['B'] * c['H']} heads of the forward [4,16,2048,64] (fp64 NumPy, {t_total:.1f} s)",
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-long", action="store_true", help="skip the reported-only long causal forward")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    a = ap.parse_args()
+    if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the per-(b, h) work would shard over GPUs with no communication).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from exact_attention_05_amd import attn_bwd, attn_fwd, attn_fwd_splitk_decode
+    from exact_attention_05_amd.binding import attn_bwd_workspace_bytes, attn_decode_workspace_bytes
+    from exact_attention_05_amd.inputs import make_tensor
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bf16 = torch.bfloat16
+
+    def mk(seed, names, B, H, N, d, scale=1.0):
+        return [make_tensor(seed, n, B, H, N, d, bf16, scale, device=dev) for n in names]
+
+    print("bench: generating inputs", file=sys.stderr, flush=True)
+    c = FWD
+    fq, fk, fv = mk(0, ("q", "k", "v"), c["B"], c["H"], c["N"], c["d"])
+    fo = torch.empty_like(fq)
+    flse = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device=dev)
+    c = DEC
+    dq_ = make_tensor(0, "q", c["B"], c["H"], 1, c["d"], bf16, device=dev)
+    dk_, dv_ = mk(0, ("k", "v"), c["B"], c["H"], c["L"], c["d"])
+    do_ = torch.empty_like(dq_)
+    dlse = torch.empty((c["B"], c["H"]), dtype=torch.float32, device=dev)
+    dws = torch.empty(attn_decode_workspace_bytes(c["B"], c["H"], c["d"], c["S"]) // 4, dtype=torch.float32,
+                      device=dev)
+    c = BWD
+    bq, bk, bv, bdo = mk(0, ("q", "k", "v", "do"), c["B"], c["H"], c["N"], c["d"])
+    bo, blse = attn_fwd(bq, bk, bv, causal=True)
+    bgq, bgk, bgv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
+    bws = torch.empty(attn_bwd_workspace_bytes(c["B"], c["H"], c["N"]) // 4, dtype=torch.float32, device=dev)
+    if not a.no_long:
+        c = FWD_LONG
+        lq, lk, lv = mk(0, ("q", "k", "v"), c["B"], c["H"], c["N"], c["d"], c["input_scale"])
+        lo = torch.empty_like(lq)
+        llse = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    print("bench: inputs resident", file=sys.stderr, flush=True)
+
+    if a.calib_copy_mib:
+        src = torch.empty(a.calib_copy_mib * 2 ** 20 // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    stream = torch.cuda.current_stream(dev)
+    names = ["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long"])
+
+    def step(ev):
+        ev["fwd"][0].record(stream)
+        attn_fwd(fq, fk, fv, causal=False, out=fo, lse=flse)
+        ev["fwd"][1].record(stream)
+        ev["decode"][0].record(stream)
+        attn_fwd_splitk_decode(dq_, dk_, dv_, DEC["S"], out=do_, lse=dlse, workspace=dws)
+        ev["decode"][1].record(stream)
+        ev["bwd"][0].record(stream)
+        attn_bwd(bq, bk, bv, bo, bdo, blse, causal=True, dq=bgq, dk=bgk, dv=bgv, workspace=bws)
+        ev["bwd"][1].record(stream)
+        if not a.no_long:
+            ev["fwd_long"][0].record(stream)
+            attn_fwd(lq, lk, lv, causal=True, out=lo, lse=llse)
+            ev["fwd_long"][1].record(stream)
+
+    def new_events():
+        return {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
+
+    for _ in range(a.warmup):
+        step(new_events())
+    torch.cuda.synchronize()
+
+    evs = [new_events() for _ in range(a.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(a.steps):
+        step(evs[i])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in evs) / a.steps for n in names}
+
+    fwd_tf = fwd_flops(FWD) / (ms["fwd"] * 1e-3) / 1e12
+    dec_gbps = dec_bytes(DEC) / (ms["decode"] * 1e-3) / 1e9
+    bwd_tf = 2.5 * fwd_flops(BWD) / (ms["bwd"] * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(fwd_tf, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(total_ms / a.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "attention forward bf16 [B=4,H=16,N=2048,d=64] non-causal (headline); split-K decode "
+                        "bf16 q[16,32,1,128] x KV[16,32,32768,128], 256 chunks; backward bf16 [2,16,4096,64] "
+                        "causal; forward bf16 [2,32,8192,128] causal (reported)",
+            "global_batch": FWD["B"],
+            "seq_len": FWD["N"],
+            "parallelism": "single GPU",
+        },
+        "fwd_pct_bf16_peak": round(100.0 * fwd_tf / PEAK_BF16_TFLOPS, 2),
+        "fwd_us": round(ms["fwd"] * 1e3, 2),
+        "decode_gbps": round(dec_gbps, 1),
+        "decode_pct_hbm": round(100.0 * dec_gbps / PEAK_HBM_GBPS, 2),
+        "decode_us": round(ms["decode"] * 1e3, 2),
+        "bwd_tflops": round(bwd_tf, 3),
+        "bwd_us": round(ms["bwd"] * 1e3, 2),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(fwd_tf, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": _traffic("fwd_bf16_d64", ["fwd.hip", "common.h"]),
+        },
+        "roofline_decode": {
+            "bound": "hbm",
+            "achieved": round(dec_gbps, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+            "traffic": _traffic("decode_d128", ["decode.hip", "common.h"]),
+        },
+    }
+    if not a.no_long:
+        lt = fwd_flops(FWD_LONG) / (ms["fwd_long"] * 1e-3) / 1e12
+        out["fwd_long_causal_tflops"] = round(lt, 3)
+        out["fwd_long_causal_us"] = round(ms["fwd_long"] * 1e3, 2)
+    if not a.no_cpu_baseline:
+        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -15,6 +15,8 @@ __all__ = [
     "attn_status_string",
     "AttnError",
     "library_path",
+    "split_decode_workspace",
+    "raw_library",
 ]
 
 

@@ -1,0 +1,202 @@
+"""ctypes binding of libattn.so; names mirror the C ABI in include/attn.h.
+
+Argument marshalling only: every arithmetic step runs in the HIP kernels.
+Torch provides device memory and the current stream.  The shared library is
+loaded on first use; when it is missing, every call raises.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libattn.so")
+_lib = None
+
+ATTN_OK = 0
+_STATUS_NAMES = {
+    0: "ATTN_OK",
+    1: "ATTN_ERR_INVALID_ARG",
+    2: "ATTN_ERR_UNSUPPORTED",
+    3: "ATTN_ERR_WORKSPACE",
+    4: "ATTN_ERR_HIP",
+}
+ATTN_F32 = 0
+ATTN_BF16 = 1
+_DTYPES = {torch.float32: ATTN_F32, torch.bfloat16: ATTN_BF16}
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(msg)
+        self.status = status
+        self.name = _STATUS_NAMES.get(status, str(status))
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is missing: build it with `python -m exact_attention_05_amd.build` "
+            "(there is no fallback implementation)"
+        )
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, ci, cf, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.attn_status_string.restype = ctypes.c_char_p
+    lib.attn_status_string.argtypes = [ci]
+    lib.attn_abi_version.restype = ci
+    lib.attn_abi_version.argtypes = []
+    lib.attn_fwd.restype = ci
+    lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.attn_decode_workspace_bytes.restype = sz
+    lib.attn_decode_workspace_bytes.argtypes = [ci, ci, ci, ci]
+    lib.attn_fwd_splitk_decode.restype = ci
+    lib.attn_fwd_splitk_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, cf, vp]
+    lib.attn_bwd_workspace_bytes.restype = sz
+    lib.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci]
+    lib.attn_bwd.restype = ci
+    lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
+    _lib = lib
+    return lib
+
+
+def raw_library():
+    """The loaded ctypes.CDLL (for ABI-level tests)."""
+    return _load()
+
+
+def attn_status_string(status):
+    return _load().attn_status_string(int(status)).decode()
+
+
+def _check(status, what):
+    if status != ATTN_OK:
+        raise AttnError(status, f"{what}: {attn_status_string(status)}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype not in _DTYPES:
+        raise AttnError(2, f"unsupported dtype {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
+def _require(cond, msg):
+    if not cond:
+        raise AttnError(1, msg)
+
+
+def _check_bhnd(name, t, shape, dtype, device):
+    _require(t.is_cuda and t.device == device, f"{name} must be on {device}")
+    _require(t.dtype == dtype, f"{name} must have dtype {dtype}")
+    _require(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
+    """O, LSE = softmax(scale Q K^T) V for [B, H, N, d] tensors on one GPU.
+
+    ``scale`` defaults to 1/sqrt(d).  Returns (o, lse) with lse [B, H, N] fp32.
+    """
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check_bhnd(name, t, (B, H, N, d), q.dtype, dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_bhnd("out", out, (B, H, N, d), q.dtype, dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    else:
+        _check_bhnd("lse", lse, (B, H, N), torch.float32, dev)
+    st = _load().attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, _dtype_code(q),
+                          scale, int(bool(causal)), _stream(dev))
+    _check(st, "attn_fwd")
+    return out, lse
+
+
+def attn_decode_workspace_bytes(B, H, d, num_splits):
+    return int(_load().attn_decode_workspace_bytes(B, H, d, num_splits))
+
+
+def attn_fwd_splitk_decode(q, k_cache, v_cache, num_splits, scale=None, out=None, lse=None, workspace=None):
+    """Split-K decode: q [B, H, 1, d] against k_cache, v_cache [B, H, L, d].
+
+    Returns (o [B, H, 1, d], lse [B, H], workspace); the workspace holds the
+    fp32 partials U [B, H, S, d], m [B, H, S], l [B, H, S] back to back.
+    """
+    B, H, one, d = q.shape
+    _require(one == 1, "q must be [B, H, 1, d]")
+    L = k_cache.shape[2]
+    dev = q.device
+    _check_bhnd("q", q, (B, H, 1, d), q.dtype, dev)
+    _check_bhnd("k_cache", k_cache, (B, H, L, d), q.dtype, dev)
+    _check_bhnd("v_cache", v_cache, (B, H, L, d), q.dtype, dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = attn_decode_workspace_bytes(B, H, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 4) + 3) // 4, dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    st = _load().attn_fwd_splitk_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                        _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                        B, H, L, d, int(num_splits), _dtype_code(q), scale, _stream(dev))
+    _check(st, "attn_fwd_splitk_decode")
+    return out, lse, workspace
+
+
+def split_decode_workspace(workspace, B, H, d, num_splits):
+    """Views (U [B, H, S, d], m [B, H, S], l [B, H, S]) of a decode workspace."""
+    S = num_splits
+    n_u = B * H * S * d
+    n_m = B * H * S
+    flat = workspace.view(-1)
+    return (flat[:n_u].view(B, H, S, d), flat[n_u:n_u + n_m].view(B, H, S),
+            flat[n_u + n_m:n_u + 2 * n_m].view(B, H, S))
+
+
+def attn_bwd_workspace_bytes(B, H, N):
+    return int(_load().attn_bwd_workspace_bytes(B, H, N))
+
+
+def attn_bwd(q, k, v, o, dO, lse, scale=None, causal=False, dq=None, dk=None, dv=None, workspace=None):
+    """dQ, dK, dV of attention from the forward's saved O and LSE.
+
+    Returns (dq, dk, dv, workspace); the workspace holds D = rowsum(dO o O).
+    """
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dO", dO)):
+        _check_bhnd(name, t, (B, H, N, d), q.dtype, dev)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32, dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    need = attn_bwd_workspace_bytes(B, H, N)
+    if workspace is None:
+        workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
+    st = _load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
+                          _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                          B, H, N, d, _dtype_code(q), scale, int(bool(causal)), _stream(dev))
+    _check(st, "attn_bwd")
+    return dq, dk, dv, workspace

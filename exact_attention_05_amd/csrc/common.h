@@ -1,0 +1,97 @@
+// Device helpers shared by the gfx950 attention kernels: vector types, MFMA
+// wrappers, bf16 conversion, exp2, the launch-order remap for the 8 XCDs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace attn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// ---------------------------------------------------------------------------
+// MFMA: D(32x32, fp32) += A(32xK) * B(Kx32).
+// Operand layout (wave64): lane l supplies row/column (l % 32) of A/B and the
+// K-slice selected by (l / 32); the accumulator element i of lane l holds
+// row 8*(i/4) + 4*(l/32) + (i%4), column l % 32.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x16 mfma32x32x16(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma32x32x2f32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Row index (within a 32-row accumulator tile) of element i in lane group g.
+__device__ __forceinline__ constexpr int acc_row(int i, int g) { return 8 * (i >> 2) + 4 * g + (i & 3); }
+
+// ---------------------------------------------------------------------------
+// bf16 <-> fp32
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Reinterpretation through memcpy: __builtin_bit_cast of a vector ELEMENT
+// (e.g. bit_cast<bf16x2>(u32x4_value[w])) is miscompiled by this hipcc (every
+// element reads element 0), so all reinterpretations go through these.
+template <typename To, typename From>
+__device__ __forceinline__ To bitcast(const From& f) {
+  static_assert(sizeof(To) == sizeof(From), "size mismatch");
+  To t;
+  __builtin_memcpy(&t, &f, sizeof(To));
+  return t;
+}
+
+__device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return bitcast<bf16x2>(w); }
+
+// Two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return bitcast<uint32_t>(v);
+}
+
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* x) {
+  u32x4 u;
+  u[0] = pack_bf16x2(x[0], x[1]);
+  u[1] = pack_bf16x2(x[2], x[3]);
+  u[2] = pack_bf16x2(x[4], x[5]);
+  u[3] = pack_bf16x2(x[6], x[7]);
+  return bitcast<bf16x8>(u);
+}
+
+// Hardware base-2 exponential (v_exp_f32); exp2(-inf) = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// log2 of a positive normal float (v_log_f32).
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ float shfl_xor_f32(float v, int mask) { return __shfl_xor(v, mask, 64); }
+
+// ---------------------------------------------------------------------------
+// Launch-order remap for 8 XCDs.
+// Consecutive workgroup ids are handed to the XCDs round-robin, and each XCD
+// has its own L2.  Mapping hardware id -> logical id so that every XCD gets a
+// contiguous range of logical ids keeps the workgroups that share one head's
+// K/V on the same L2.  It is a bijection on [0, total) for any total.
+// ---------------------------------------------------------------------------
+constexpr int kNumXcd = 8;
+
+__device__ __forceinline__ int xcd_remap(int hw_id, int total) {
+  const int xcd = hw_id % kNumXcd;
+  const int slot = hw_id / kNumXcd;
+  const int q = total / kNumXcd;
+  const int r = total % kNumXcd;
+  return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+}  // namespace attn

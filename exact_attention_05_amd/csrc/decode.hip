@@ -1,0 +1,257 @@
+// FlashDecoding split-K decode for gfx950: one query row per (b, h) against a
+// long K/V cache (cnblogs article on FlashAttention tiling, section 3
+// scenario B; "FlashAttention 1 和 FlashAttention 2 的区别", sections 6 and 13).
+//
+// Map step (decode_partial_kernel): one workgroup per (b*h, chunk).  A chunk
+// is streamed once from HBM with 16-byte loads issued R keys at a time per
+// lane (all loads of a round in flight together); each group of D/8 lanes
+// owns one key at a time, forms q.k with bf16 dot2 instructions and a
+// cross-lane sum, and keeps a running (m, l, U) over its keys.  The states of
+// the key groups are merged across lanes and then across the 4 wavefronts
+// with the partial-state merge, and the chunk's (U, m, l) is written to the
+// workspace.  This is HBM-bandwidth work: no MFMA (a single query row).
+//
+// Reduce step (decode_merge_kernel): one workgroup per (b, h) merges its S
+// partials: m = max m_c, l = sum e^(m_c - m) l_c, U = sum e^(m_c - m) U_c,
+// O = U / l, LSE = m + ln l.
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kRound = 8;  // keys per lane group per round (loads in flight)
+
+struct State {
+  float m;  // running max, log2 units of the scaled score
+  float l;
+  float u[8];
+};
+
+// Merge state `o` into `s` (both in log2 units); -inf states carry weight 0.
+__device__ __forceinline__ void merge_into(State& s, const State& o) {
+  const float mn = fmaxf(s.m, o.m);
+  const float ms = (mn == kNegInf) ? 0.f : mn;
+  const float a = fast_exp2(s.m - ms);
+  const float b = fast_exp2(o.m - ms);
+  s.l = a * s.l + b * o.l;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) s.u[e] = a * s.u[e] + b * o.u[e];
+  s.m = mn;
+}
+
+__device__ __forceinline__ State shfl_state(const State& s, int mask) {
+  State o;
+  o.m = shfl_xor_f32(s.m, mask);
+  o.l = shfl_xor_f32(s.l, mask);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o.u[e] = shfl_xor_f32(s.u[e], mask);
+  return o;
+}
+
+__device__ __forceinline__ float dot8_bf16(const u32x4& a, const u32x4& b) {
+  float acc = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t aw = a[w], bw = b[w];
+    acc = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(aw), as_bf16x2(bw), acc, false);
+  }
+  return acc;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_partial_kernel(const __bf16* __restrict__ Q,
+                                                                  const __bf16* __restrict__ K,
+                                                                  const __bf16* __restrict__ V,
+                                                                  float* __restrict__ ws, int L, int S,
+                                                                  int BH, float scale_log2) {
+  constexpr int LPK = D / 8;       // lanes per key (8 bf16 each)
+  constexpr int SPW = 64 / LPK;    // key slots per wavefront
+  constexpr int NS = SPW * kWaves; // key slots per workgroup
+  __shared__ float sm_u[kWaves][D];
+  __shared__ float sm_ml[kWaves][2];
+
+  const int id = blockIdx.x;
+  const int bh = id / S;
+  const int c = id % S;
+  const int lo = (int)(((int64_t)c * L) / S);
+  const int hi = (int)(((int64_t)(c + 1) * L) / S);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int u = lane % LPK;                    // d chunk: dims 8u .. 8u+7
+  const int slot = wave * SPW + lane / LPK;    // key slot in the workgroup
+
+  const __bf16* Kh = K + (int64_t)bh * L * D;
+  const __bf16* Vh = V + (int64_t)bh * L * D;
+  const u32x4 qv = *reinterpret_cast<const u32x4*>(Q + (int64_t)bh * D + 8 * u);
+
+  State st;
+  st.m = kNegInf;
+  st.l = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) st.u[e] = 0.f;
+
+  for (int k0 = lo; k0 < hi; k0 += NS * kRound) {
+    u32x4 kr[kRound], vr[kRound];
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      const int key = k0 + r * NS + slot;
+      const bool ok = key < hi;
+      kr[r] = ok ? *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + 8 * u) : u32x4{};
+      vr[r] = ok ? *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + 8 * u) : u32x4{};
+    }
+    float s[kRound];
+    float rmax = kNegInf;
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      float x = dot8_bf16(qv, kr[r]);
+#pragma unroll
+      for (int msk = 1; msk < LPK; msk <<= 1) x += shfl_xor_f32(x, msk);
+      const int key = k0 + r * NS + slot;
+      s[r] = key < hi ? x * scale_log2 : kNegInf;
+      rmax = fmaxf(rmax, s[r]);
+    }
+    const float mn = fmaxf(st.m, rmax);
+    const float ms = (mn == kNegInf) ? 0.f : mn;
+    const float alpha = fast_exp2(st.m - ms);
+    st.l *= alpha;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) st.u[e] *= alpha;
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      const float p = fast_exp2(s[r] - ms);
+      st.l += p;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        st.u[2 * w] = fmaf(p, bf16lo_to_f32(vr[r][w]), st.u[2 * w]);
+        st.u[2 * w + 1] = fmaf(p, bf16hi_to_f32(vr[r][w]), st.u[2 * w + 1]);
+      }
+    }
+    st.m = mn;
+  }
+
+  // merge the key slots of this wavefront (lanes with equal u)
+#pragma unroll
+  for (int msk = LPK; msk < 64; msk <<= 1) {
+    const State o = shfl_state(st, msk);
+    merge_into(st, o);
+  }
+  if (lane < LPK) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm_u[wave][8 * u + e] = st.u[e];
+    if (lane == 0) {
+      sm_ml[wave][0] = st.m;
+      sm_ml[wave][1] = st.l;
+    }
+  }
+  __syncthreads();
+
+  // merge the 4 wavefronts and write U [bh][c][d], m [bh][c], l [bh][c]
+  if (tid < D) {
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm_ml[w][0]);
+    const float Ms = (M == kNegInf) ? 0.f : M;
+    float acc = 0.f, lt = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float wt = fast_exp2(sm_ml[w][0] - Ms);
+      acc += wt * sm_u[w][tid];
+      lt += wt * sm_ml[w][1];
+    }
+    const int64_t pc = (int64_t)bh * S + c;
+    ws[pc * D + tid] = acc;
+    if (tid == 0) {
+      float* wm = ws + (int64_t)BH * S * D;
+      float* wl = wm + (int64_t)BH * S;
+      wm[pc] = (M == kNegInf) ? kNegInf : M * kLn2;
+      wl[pc] = lt;
+    }
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void decode_merge_kernel(const float* __restrict__ ws, __bf16* __restrict__ O,
+                                                                float* __restrict__ LSE, int S, int BH) {
+  constexpr int G = kThreads / D;  // chunk groups working on the same d
+  __shared__ float sm_w[kThreads];
+  __shared__ float sm_red[kThreads];
+  __shared__ float sm_acc[G][D];
+
+  const int bh = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* wu = ws + (int64_t)bh * S * D;
+  const float* wm = ws + (int64_t)BH * S * D + (int64_t)bh * S;
+  const float* wl = ws + (int64_t)BH * S * D + (int64_t)BH * S + (int64_t)bh * S;
+
+  // M = max_c m_c
+  float mx = kNegInf;
+  for (int c = tid; c < S; c += kThreads) mx = fmaxf(mx, wm[c]);
+  sm_red[tid] = mx;
+  __syncthreads();
+  for (int st = kThreads / 2; st > 0; st >>= 1) {
+    if (tid < st) sm_red[tid] = fmaxf(sm_red[tid], sm_red[tid + st]);
+    __syncthreads();
+  }
+  const float M = sm_red[0];
+  const float Ms = (M == kNegInf) ? 0.f : M;
+  __syncthreads();
+
+  const int grp = tid / D, d = tid % D;
+  float acc = 0.f, lpart = 0.f;
+  for (int c0 = 0; c0 < S; c0 += kThreads) {
+    const int c = c0 + tid;
+    float w = 0.f;
+    if (c < S) {
+      const float mc = wm[c];
+      w = (mc == kNegInf) ? 0.f : fast_exp2((mc - Ms) * kLog2e);
+      lpart += w * wl[c];
+    }
+    sm_w[tid] = w;
+    __syncthreads();
+    const int n = min(kThreads, S - c0);
+    for (int cc = grp; cc < n; cc += G) acc += sm_w[cc] * wu[(int64_t)(c0 + cc) * D + d];
+    __syncthreads();
+  }
+  sm_acc[grp][d] = acc;
+  sm_red[tid] = lpart;
+  __syncthreads();
+  for (int st = kThreads / 2; st > 0; st >>= 1) {
+    if (tid < st) sm_red[tid] += sm_red[tid + st];
+    __syncthreads();
+  }
+  const float lt = sm_red[0];
+  if (tid < D) {
+    float u = 0.f;
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) u += sm_acc[gi][tid];
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    O[(int64_t)bh * D + tid] = (__bf16)(u * inv);
+    if (tid == 0 && LSE != nullptr) LSE[bh] = lt > 0.f ? M + fast_log2(lt) * kLn2 : kNegInf;
+  }
+}
+
+template <int D>
+hipError_t run_decode(const DecodeArgs& a, hipStream_t s) {
+  const int BH = a.B * a.H;
+  const int64_t nwg = (int64_t)BH * a.splits;
+  hipLaunchKernelGGL((decode_partial_kernel<D>), dim3((unsigned)nwg), dim3(kThreads), 0, s,
+                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                     static_cast<const __bf16*>(a.v), a.ws, a.L, a.splits, BH, a.scale * kLog2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(BH), dim3(kThreads), 0, s, a.ws, static_cast<__bf16*>(a.o),
+                     a.lse, a.splits, BH);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
+  return a.d == 64 ? run_decode<64>(a, s) : run_decode<128>(a, s);
+}
+
+}  // namespace attn

@@ -1,0 +1,55 @@
+// Host-side launchers of the attention kernels.  Each returns the HIP error
+// of its launch(es); shapes have been validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace attn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  int B, H, N, d;
+  float scale;
+  int causal;
+};
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;  // may be null
+  float* ws;   // U [BH][S][d], m [BH][S], l [BH][S]
+  int B, H, L, d, splits;
+  float scale;
+};
+
+hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dO;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* delta;  // [B*H*N] workspace
+  int B, H, N, d;
+  float scale;
+  int causal;
+};
+
+hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+
+}  // namespace attn

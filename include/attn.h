@@ -1,0 +1,161 @@
+/*
+ * attn.h -- C ABI of libattn.so: exact attention on AMD MI355X (gfx950).
+ *
+ * Three operations, each an FA-2 style tiled computation that never writes
+ * the N x N score or probability matrix to device memory:
+ *
+ *   attn_fwd                O = softmax(scale * Q K^T) V and the per-row
+ *                           log-sum-exp.
+ *   attn_fwd_splitk_decode  the same for a single query row against a long
+ *                           key/value cache, split into chunks whose partial
+ *                           (U, m, l) states are merged afterwards.
+ *   attn_bwd                dQ, dK, dV by recomputing P from the saved LSE.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, owned by the caller.  The
+ *     library never allocates, frees or retains them beyond the call.
+ *   - Tensors are dense, row-major [B, H, rows, d] with d fastest
+ *     (the [batch, heads, sequence, head_dim] layout of PyTorch's
+ *     scaled_dot_product_attention, described on the "FlashAttention" page of
+ *     xuesongtap.github.io, section 6), and 16-byte aligned.
+ *   - Every call only enqueues kernels on `stream` (a hipStream_t; NULL is the
+ *     null stream) and returns; the caller synchronises.  Argument checks run
+ *     on the host before any HIP call, so an error status means nothing was
+ *     launched.  No C++ exception crosses the ABI.
+ *   - `scale` multiplies Q K^T before the softmax and must be finite and > 0;
+ *     the usual value is 1/sqrt(d).
+ *   - `causal` != 0 masks key index j > query index i (square problem,
+ *     top-left aligned): "FlashAttention" (xuesongtap), section 2.2.
+ *   - LSE values are natural-log log-sum-exp of the scaled scores,
+ *     LSE_i = m_i + ln(l_i) (xuesongtap, section 3), stored as fp32.
+ *   - Supported: dtype ATTN_BF16 with d in {64, 128}; dtype ATTN_F32 with
+ *     d == 64 (forward only).  Other combinations return
+ *     ATTN_ERR_UNSUPPORTED.  Accumulation is always fp32; outputs in the
+ *     input dtype are rounded to nearest even.
+ */
+#ifndef ATTN_H
+#define ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ATTN_OK = 0,
+  ATTN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad scale */
+  ATTN_ERR_UNSUPPORTED = 2, /* dtype/head_dim combination not built */
+  ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  ATTN_ERR_HIP = 4          /* a HIP launch reported an error */
+} attn_status;
+
+typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* attn_status_string(attn_status s);
+
+/* Version of this ABI (incremented on incompatible changes). */
+int attn_abi_version(void);
+
+/*
+ * attn_fwd -- exact attention forward.
+ *
+ * Computes, per (b, h), S = scale * Q K^T (masked if causal), P = softmax(S)
+ * row-wise, O = P V, and LSE_i = log sum_j exp(S_ij): the definition in
+ * "FlashAttention" (xuesongtap), section 1, evaluated with the FA-2 loop of
+ * its sections 2.1-2.2 (outer loop over query tiles kept on chip, inner loop
+ * over K/V tiles with the running state (m, l, U), O = U / l at the end) and
+ * the LSE of its section 3.
+ *
+ *   q, k, v : [B, H, N, d] in `dtype` (read only)
+ *   o       : [B, H, N, d] in `dtype` (written)
+ *   lse     : [B, H, N] fp32 (written; may be NULL when not needed)
+ *   B, H, N : >= 1;  B*H <= 2^31-1, N <= 2^24
+ *
+ * Errors: ATTN_ERR_INVALID_ARG for a NULL or non-16-byte-aligned q/k/v/o, a
+ * 4-byte-misaligned lse, a size out of range or a bad scale;
+ * ATTN_ERR_UNSUPPORTED for an unsupported (dtype, d);  ATTN_ERR_HIP when the
+ * launch fails.
+ */
+attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                     int B, int H, int N, int d, attn_dtype dtype, float scale, int causal,
+                     void* stream);
+
+/*
+ * Workspace size in bytes that attn_fwd_splitk_decode needs for the given
+ * shape: B*H*num_splits*(d + 2) fp32 values.  Returns 0 for invalid sizes.
+ */
+size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits);
+
+/*
+ * attn_fwd_splitk_decode -- FlashDecoding split-K attention for one query
+ * row per (b, h).
+ *
+ * The cache of length L is cut into `num_splits` chunks; chunk c covers keys
+ * [floor(c*L/S), floor((c+1)*L/S)).  For each chunk a partial state is
+ * computed (the map step of FlashDecoding, cnblogs article on FlashAttention
+ * tiling, section 3 scenario B; the partial (m, l, O) of "FlashAttention 1 和
+ * FlashAttention 2 的区别", section 6):
+ *     m_c = max_j s_j,  l_c = sum_j e^(s_j - m_c),  U_c = sum_j e^(s_j - m_c) V_j
+ * with s = scale * K_c q, and the partials are merged (the reduce step):
+ *     m = max_c m_c, l = sum_c e^(m_c - m) l_c, U = sum_c e^(m_c - m) U_c,
+ *     O = U / l,  LSE = m + ln l.
+ * An empty chunk (S > L) has m_c = -inf, l_c = 0, U_c = 0 and weight 0.
+ * There is no causal flag: the single query sees the whole cache.
+ *
+ *   q        : [B, H, 1, d] in `dtype`
+ *   k_cache  : [B, H, L, d] in `dtype`;  v_cache : [B, H, L, d]
+ *   o        : [B, H, 1, d] in `dtype` (written)
+ *   lse      : [B, H] fp32 (written; may be NULL)
+ *   workspace: device buffer of at least attn_decode_workspace_bytes(...)
+ *              bytes, 16-byte aligned.  On return (after the stream
+ *              completes) it holds the partials, fp32, in this order:
+ *              U [B, H, S, d], then m [B, H, S] (natural-log units of the
+ *              scaled score), then l [B, H, S].
+ *   num_splits: 1 <= S <= 65535.
+ *
+ * Supported: ATTN_BF16 with d in {64, 128}.
+ * Errors as attn_fwd, plus ATTN_ERR_WORKSPACE for a NULL or short workspace.
+ */
+attn_status attn_fwd_splitk_decode(const void* q, const void* k_cache, const void* v_cache,
+                                   void* o, float* lse, void* workspace, size_t workspace_bytes,
+                                   int B, int H, int L, int d, int num_splits, attn_dtype dtype,
+                                   float scale, void* stream);
+
+/*
+ * Workspace size in bytes that attn_bwd needs: the fp32 vector
+ * D = rowsum(dO o O), B*H*N values.  Returns 0 for invalid sizes.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int N);
+
+/*
+ * attn_bwd -- exact attention backward by recomputation.
+ *
+ * With P rebuilt tile by tile as P_ij = exp(S_ij - LSE_i) from the saved LSE
+ * ("8. FlashAttention 实战", triton-tutorial.pages.dev, section 8.8.2), and
+ * D_i = sum_d dO_i o O_i from the saved O (section 8.8.3):
+ *     dV = P^T dO,  dP = dO V^T,  dS = P o (dP - D),
+ *     dQ = scale * dS K,  dK = scale * dS^T Q          (sections 8.8.1, 8.8.3)
+ * computed in two deterministic phases without atomics (section 8.8.4):
+ * dK/dV with key tiles outer, then dQ with query tiles outer.
+ *
+ *   q, k, v, o, dO : [B, H, N, d] in `dtype` (o is attn_fwd's output)
+ *   lse            : [B, H, N] fp32 from attn_fwd with the same arguments
+ *   dq, dk, dv     : [B, H, N, d] in `dtype` (written)
+ *   workspace      : >= attn_bwd_workspace_bytes(B, H, N) bytes, 16-byte
+ *                    aligned; holds D on return.
+ *
+ * Supported: ATTN_BF16 with d in {64, 128}.
+ * Errors as attn_fwd, plus ATTN_ERR_WORKSPACE.
+ */
+attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                     const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                     size_t workspace_bytes, int B, int H, int N, int d, attn_dtype dtype,
+                     float scale, int causal, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_H */
