@@ -36,6 +36,9 @@ COMMON_FLAGS = [
     "-std=c++17",
     "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: avoids v_accvgpr_read/write copies
+    # around every softmax step (gfx950 has one unified register file).
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

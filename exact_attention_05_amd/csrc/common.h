@@ -78,6 +78,31 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 __device__ __forceinline__ float shfl_xor_f32(float v, int mask) { return __shfl_xor(v, mask, 64); }
 
 // ---------------------------------------------------------------------------
+// LDS access helpers (gfx950)
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// Direct HBM -> LDS copy of 16 bytes per lane: lane l's bytes land at
+// lds_base + 16 * l (lds_base must be the same for the whole wavefront).
+__device__ __forceinline__ void global_to_lds16(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_base, 16, 0, 0);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within every group of 16 lanes,
+// each lane names 8 bytes (4 consecutive 16-bit values); lane i of the group
+// receives, as its element j, element (i % 4) of the 8 bytes named by lane
+// 4 * j + i / 4 of the group.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_addr) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)lds_addr);
+  return bitcast<u32x2>(v);
+}
+
+// Wait until every memory operation this wavefront issued has completed
+// (including direct-to-LDS copies).
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ---------------------------------------------------------------------------
 // Launch-order remap for 8 XCDs.
 // Consecutive workgroup ids are handed to the XCDs round-robin, and each XCD
 // has its own L2.  Mapping hardware id -> logical id so that every XCD gets a

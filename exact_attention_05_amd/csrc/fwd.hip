@@ -34,34 +34,62 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBc = 64;  // keys per K/V tile
-constexpr int kPad = 8;  // bf16 elements of LDS row padding (16 bytes)
 
+// K/V tile layout in LDS.  A tile of 64 keys x D bf16 is stored row-major
+// (key k, dims d) as a sequence of 256-byte lines -- 64 banks of 4 bytes --
+// and the 16-byte chunks inside a line are XOR-swizzled by a function of the
+// line index.  The swizzle is chosen so that
+//   * the K operand reads (16 consecutive keys, one chunk each) and
+//   * the transposing V reads (4 consecutive keys x 2 chunks x 2 halves)
+// of every 16-lane group touch 16 distinct bank groups.
+// d = 64: key k lives in line k/2, chunks 8*(k%2) .. 8*(k%2)+7.
+// d = 128: key k is line k.
 template <int D>
-struct FwdLds {
-  static constexpr int kKRow = D + kPad;    // K tile: [64 keys][D], row stride
-  static constexpr int kVRow = kBc + kPad;  // V^T tile: [D][64 keys], row stride
-  static constexpr int kKElems = kBc * kKRow;
-  static constexpr int kVElems = D * kVRow;
-  static constexpr int kBufElems = kKElems + kVElems;
-  static constexpr int kElems = 2 * kBufElems;
+struct TileLayout {
+  static constexpr int kLines = D / 2;        // 256-byte lines per tile
+  static constexpr int kBytes = kLines * 256;  // = 64 * D * 2
+  __device__ static __forceinline__ int swz(int line) {
+    if constexpr (D == 64) return ((line & 1) << 1) | ((line >> 1) & 1) | (line & 4);
+    else return ((line & 3) << 1) | ((line >> 2) & 1) | (line & 8);
+  }
+  // byte offset of logical 16-byte chunk c of key k
+  __device__ static __forceinline__ int offset(int k, int c) {
+    const int lin = k * (D * 2) + 16 * c;  // unswizzled byte offset
+    const int line = lin >> 8;
+    const int chunk = (lin >> 4) & 15;
+    return line * 256 + 16 * (chunk ^ swz(line));
+  }
+  // inverse: the (key, chunk) stored at physical chunk p of line `line`
+  __device__ static __forceinline__ void at(int line, int p, int& k, int& c) {
+    const int chunk = p ^ swz(line);
+    const int lin = line * 256 + 16 * chunk;
+    k = lin / (D * 2);
+    c = (lin % (D * 2)) / 16;
+  }
 };
 
-// Position of 4-key chunk kc inside the transposed V tile.  Within every
-// 16-key group the accumulator supplies keys {0-3, 8-11} to lanes 0-31 and
-// {4-7, 12-15} to lanes 32-63 of one MFMA; swapping the two low bits of the
-// chunk index makes each of those sets 8 contiguous columns.
-__device__ __forceinline__ int vt_chunk(int kc) { return (kc & ~3) | ((kc & 1) << 1) | ((kc >> 1) & 1); }
+// Reference point of the exponentials.  The online state (m, l, U) is exact
+// for ANY reference m as long as l, U and the LSE all use the same one
+// (O = U / l and LSE = m + ln l cancel it), and numerically m only has to keep
+// every P~ = 2^(s*c - m) finite.  So m is set to the exact row max on the
+// first K/V tile and afterwards moves only when a lane's partial row sum of a
+// tile exceeds kSumLimit (or overflows): then the tile's exponentials are
+// redone with the exact running max, U and l rescaled, as in the plain online
+// update.  For ordinary inputs that never happens after the first tile, which
+// removes the per-tile row max and the rescale of U from the inner loop.
+// With partial sums below 2^64, U stays below 2^64 * N * max|v|.
+constexpr float kSumLimit = 18446744073709551616.f;  // 2^64
 
 template <int D, int QT, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg,
     float scale_log2) {
-  using L = FwdLds<D>;
+  using T = TileLayout<D>;
   constexpr int BR = kWaves * 32 * QT;
-  constexpr int KCH = kBc * D / 8 / kThreads;   // 16-byte K chunks per thread
-  constexpr int VBL = kBc * D / 16 / kThreads;  // 4x4 V blocks per thread
-  __shared__ __attribute__((aligned(16))) __bf16 smem[L::kElems];
+  constexpr int NLD = D / 32;  // direct-to-LDS copies per wavefront per tile and tensor
+  // two buffers, each a K tile then a V tile
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * T::kBytes];
 
   const int lid = xcd_remap(blockIdx.x, total_wg);
   const int bh = lid / n_qtiles;
@@ -107,135 +135,151 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
     for (int mt = 0; mt < D / 32; ++mt) oacc[nt][mt] = f32x16{};
   }
 
-  u32x4 kreg[KCH];
-  u32x2 vreg[VBL][4];
-
-  auto gload = [&](int kb) {
+  // Copy geometry: copy i of this wavefront fills lines 4*(wave*NLD + i) ..
+  // +3 of a tile; lane l fills physical chunk l%16 of line +l/16, i.e. the
+  // logical (key, chunk) that the swizzle maps there.
+  int ld_key[NLD], ld_col[NLD];
 #pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int id = tid + c * kThreads;
-      const int row = id / (D / 8), col = (id % (D / 8)) * 8;
-      const int key = kb + row;
-      kreg[c] = key < N ? *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + col) : u32x4{};
-    }
-#pragma unroll
-    for (int b = 0; b < VBL; ++b) {
-      const int id = tid + b * kThreads;
-      const int kc = id / (D / 4), dc = id % (D / 4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = kb + 4 * kc + r;
-        vreg[b][r] = key < N ? *reinterpret_cast<const u32x2*>(Vh + (int64_t)key * D + 4 * dc) : u32x2{};
-      }
-    }
-  };
-
-  auto sstore = [&](int buf) {
-    __bf16* Ks = smem + buf * L::kBufElems;
-    __bf16* Vt = Ks + L::kKElems;
-#pragma unroll
-    for (int c = 0; c < KCH; ++c) {
-      const int id = tid + c * kThreads;
-      const int row = id / (D / 8), col = (id % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(Ks + row * L::kKRow + col) = kreg[c];
-    }
-#pragma unroll
-    for (int b = 0; b < VBL; ++b) {
-      const int id = tid + b * kThreads;
-      const int kc = id / (D / 4), dc = id % (D / 4);
-      const int pcol = 4 * vt_chunk(kc);
-      // 4 keys x 4 dims -> 4 dims x 4 keys (bf16 pairs)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int w = i >> 1;
-        const bool hi = i & 1;
-        uint32_t e[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) e[r] = hi ? (vreg[b][r][w] >> 16) : (vreg[b][r][w] & 0xffffu);
-        u32x2 out = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-        *reinterpret_cast<u32x2*>(Vt + (4 * dc + i) * L::kVRow + pcol) = out;
-      }
-    }
-  };
-
-  if (nblk > 0) {
-    gload(0);
-    sstore(0);
+  for (int i = 0; i < NLD; ++i) {
+    const int line = 4 * (wave * NLD + i) + (lane >> 4);
+    int k, c;
+    T::at(line, lane & 15, k, c);
+    ld_key[i] = k;
+    ld_col[i] = 8 * c;
   }
+  auto issue_tile_copy = [&](int kb, int buf) {
+    unsigned char* kt = smem + buf * 2 * T::kBytes;
+    unsigned char* vt = kt + T::kBytes;
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      // rows past the end read row N-1 (valid memory); they are masked out
+      const int row = min(kb + ld_key[i], N - 1);
+      const int64_t off = (int64_t)row * D + ld_col[i];
+      const int lds_line = 4 * (wave * NLD + i);
+      global_to_lds16(Kh + off, kt + lds_line * 256);
+      global_to_lds16(Vh + off, vt + lds_line * 256);
+    }
+  };
+
+  // Per-lane LDS read offsets.
+  // K operand of S^T = K Q^T: key 32kh + l32, chunk 2ks + g.
+  int koff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = T::offset(l32, 2 * ks + g);
+  constexpr int kKhStep = 32 * D * 2;  // 32 keys further: same swizzle phase
+  // V^T operand of O^T += V^T P~^T through transposing reads: source lane
+  // s = lane%16 of group G = lane/16 names key 16t + 8h + 4(G/2) + s/4 and
+  // dims 32mt + 16(G%2) + 4(s%4) .. +3.
+  int voff[2][D / 32];
+  {
+    const int s = lane & 15, G = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) {
+        const int key = 8 * h + 4 * (G >> 1) + (s >> 2);
+        const int dim = 32 * mt + 16 * (G & 1) + 4 * (s & 3);
+        voff[h][mt] = T::offset(key, dim >> 3) + 8 * ((dim >> 2) & 1);
+      }
+  }
+  constexpr int kTStep = 16 * D * 2;  // 16 keys further: same swizzle phase
+
+  f32x16 sacc[QT][2];
+
+  // S^T = K_j Q^T for the tile in LDS at kt, masked where needed.
+  auto scores = [&](const unsigned char* kt, int kb) {
+#pragma unroll
+    for (int nt = 0; nt < QT; ++nt) sacc[nt][0] = sacc[nt][1] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+#pragma unroll
+      for (int kh = 0; kh < 2; ++kh) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[ks] + kh * kKhStep);
+#pragma unroll
+        for (int nt = 0; nt < QT; ++nt) sacc[nt][kh] = mfma32x32x16(a, qf[nt][ks], sacc[nt][kh]);
+      }
+    }
+    const bool need_mask = (kb + kBc > N) || (CAUSAL && kb + kBc - 1 > qw0);
+    if (need_mask) {
+#pragma unroll
+      for (int nt = 0; nt < QT; ++nt) {
+        const int qr = qw0 + nt * 32 + l32;
+#pragma unroll
+        for (int kh = 0; kh < 2; ++kh) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb + 32 * kh + acc_row(i, g);
+            const bool vis = key < N && (!CAUSAL || key <= qr);
+            if (!vis) sacc[nt][kh][i] = kNegInf;
+          }
+        }
+      }
+    }
+  };
+
+  // Exact running max of the raw scores of query tile nt: m moves up to it,
+  // U and l are rescaled by alpha = 2^(m_old - m_new) (0 while m_old = -inf).
+  auto exact_max_update = [&](int nt) {
+    float t8[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      t8[e] = fmaxf(fmaxf(sacc[nt][e >> 2][4 * (e & 3)], sacc[nt][e >> 2][4 * (e & 3) + 1]),
+                    fmaxf(sacc[nt][e >> 2][4 * (e & 3) + 2], sacc[nt][e >> 2][4 * (e & 3) + 3]));
+    float mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])),
+                     fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    const float mx2 = mx * scale_log2;
+    const bool grow = mx2 > m2[nt];
+    const float alpha = grow ? fast_exp2(m2[nt] - mx2) : 1.f;
+    m2[nt] = grow ? mx2 : m2[nt];
+    lsum[nt] *= alpha;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) oacc[nt][mt] *= alpha;
+  };
+
+  // P~ = 2^(s*c - m) of query tile nt, rounded to bf16 straight into the B
+  // operands of the second product (the raw scores stay in sacc); rs gets the
+  // lane's fp32 partial row sum.  Returns whether that sum is too large.
+  float rs[QT];
+  bf16x8 pb[QT][4];
+  auto exponentials = [&](int nt) {
+    const float msafe = (m2[nt] == kNegInf) ? 0.f : m2[nt];
+    float r4[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = fast_exp2(fmaf(sacc[nt][t >> 1][8 * (t & 1) + e], scale_log2, -msafe));
+      r4[t] = ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+      pb[nt][t] = pack_bf16x8(x);
+    }
+    rs[nt] = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+    return !(rs[nt] <= kSumLimit);
+  };
+
+  if (nblk > 0) issue_tile_copy(0, 0);
+  wait_all_memory();
   __syncthreads();
 
   for (int j = 0; j < nblk; ++j) {
     const int kb = j * kBc;
     const int buf = j & 1;
-    if (j + 1 < nblk) gload(kb + kBc);
-    const __bf16* Ks = smem + buf * L::kBufElems;
-    const __bf16* Vt = Ks + L::kKElems;
+    if (j + 1 < nblk) issue_tile_copy(kb + kBc, buf ^ 1);
+    const unsigned char* kt = smem + buf * 2 * T::kBytes;
+    const unsigned char* vt = kt + T::kBytes;
 
     const bool active = !CAUSAL || kb <= qw0 + 32 * QT - 1;
     if (active) {
-      // S^T = K_j Q^T: [64 keys] x [32 queries] per (kh, nt)
-      f32x16 sacc[QT][2];
-#pragma unroll
-      for (int nt = 0; nt < QT; ++nt) sacc[nt][0] = sacc[nt][1] = f32x16{};
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Ks + (32 * kh + l32) * L::kKRow + 16 * ks + 8 * g);
-#pragma unroll
-          for (int nt = 0; nt < QT; ++nt) sacc[nt][kh] = mfma32x32x16(a, qf[nt][ks], sacc[nt][kh]);
-        }
-      }
-
-      const bool need_mask = (kb + kBc > N) || (CAUSAL && kb + kBc - 1 > qw0);
-      if (need_mask) {
-#pragma unroll
-        for (int nt = 0; nt < QT; ++nt) {
-          const int qr = qw0 + nt * 32 + l32;
-#pragma unroll
-          for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = kb + 32 * kh + acc_row(i, g);
-              const bool vis = key < N && (!CAUSAL || key <= qr);
-              if (!vis) sacc[nt][kh][i] = kNegInf;
-            }
-          }
-        }
-      }
-
-      bf16x8 pb[QT][4];
+      scores(kt, kb);
 #pragma unroll
       for (int nt = 0; nt < QT; ++nt) {
-        float mx = kNegInf;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[nt][kh][i]);
-        mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-        const float mnew = fmaxf(m2[nt], mx * scale_log2);
-        const float msafe = (mnew == kNegInf) ? 0.f : mnew;
-        const float alpha = fast_exp2(m2[nt] - msafe);
-        m2[nt] = mnew;
-        float rs = 0.f;
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(fmaf(sacc[nt][kh][i], scale_log2, -msafe));
-            sacc[nt][kh][i] = p;
-            rs += p;
-          }
-        lsum[nt] = lsum[nt] * alpha + rs;
-#pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt) oacc[nt][mt] *= alpha;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          float x[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) x[e] = sacc[nt][t >> 1][8 * (t & 1) + e];
-          pb[nt][t] = pack_bf16x8(x);
+        if (j == 0) exact_max_update(nt);
+        if (__ballot(exponentials(nt))) {
+          // rare: the reference fell too far below this tile's scores
+          exact_max_update(nt);
+          exponentials(nt);
         }
+        lsum[nt] += rs[nt];
       }
 
       // O^T += V_j^T P~^T
@@ -243,18 +287,21 @@ __global__ __launch_bounds__(kThreads) void fwd_bf16_kernel(
       for (int t = 0; t < 4; ++t) {
 #pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Vt + (32 * mt + l32) * L::kVRow + 16 * t + 8 * g);
+          const u32x2 lo = lds_read_tr16(vt + voff[0][mt] + t * kTStep);
+          const u32x2 hi = lds_read_tr16(vt + voff[1][mt] + t * kTStep);
+          const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+          const bf16x8 a = bitcast<bf16x8>(w);
 #pragma unroll
           for (int nt = 0; nt < QT; ++nt) oacc[nt][mt] = mfma32x32x16(a, pb[nt][t], oacc[nt][mt]);
         }
       }
     }
 
-    if (j + 1 < nblk) sstore(buf ^ 1);
+    wait_all_memory();
     __syncthreads();
   }
 
-  // Epilogue: O = U / l (bf16, RNE) and LSE = (m2 + log2 l) * ln 2.
+  // Epilogue: O = U / l (bf16, RNE) and LSE = (m + log2 l) * ln 2.
 #pragma unroll
   for (int nt = 0; nt < QT; ++nt) {
     const int qr = qw0 + nt * 32 + l32;
@@ -457,7 +504,7 @@ hipError_t run_f32(const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
-  if (a.d == 64) return a.causal ? run_bf16<64, 1, true>(a, s) : run_bf16<64, 1, false>(a, s);
+  if (a.d == 64) return a.causal ? run_bf16<64, 2, true>(a, s) : run_bf16<64, 2, false>(a, s);
   return a.causal ? run_bf16<128, 1, true>(a, s) : run_bf16<128, 1, false>(a, s);
 }
 
