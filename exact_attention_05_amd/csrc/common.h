@@ -102,6 +102,27 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds_addr) {
 // (including direct-to-LDS copies).
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Workgroup barrier for LDS hand-offs that must not wait on the wavefront's
+// outstanding global->LDS copies (__syncthreads() would, through its
+// workgroup-scope fences).  Callers make their own copies complete with
+// wait_vm_at_most before it.  LDS reads issued before it have returned
+// (lgkmcnt(0)), and the asm clobbers keep the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) only
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most N vector-memory operations of this wavefront are
+// outstanding (s_waitcnt vmcnt(N); LDS and export counters not waited on).
+template <int N>
+__device__ __forceinline__ void wait_vm_at_most() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // ---------------------------------------------------------------------------
 // Launch-order remap for 8 XCDs.
 // Consecutive workgroup ids are handed to the XCDs round-robin, and each XCD

@@ -80,7 +80,7 @@ struct TileLayout {
 // With partial sums below 2^64, U stays below 2^64 * N * max|v|.
 constexpr float kSumLimit = 18446744073709551616.f;  // 2^64
 
-template <int D, int QT, bool CAUSAL>
+template <int D, int QT, int NBUF, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg,
@@ -88,8 +88,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   using T = TileLayout<D>;
   constexpr int BR = kWaves * 32 * QT;
   constexpr int NLD = D / 32;  // direct-to-LDS copies per wavefront per tile and tensor
-  // two buffers, each a K tile then a V tile
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * 2 * T::kBytes];
+  // A ring of NBUF buffers, each a K tile then a V tile; tile j uses buffer
+  // j % NBUF and is copied NBUF - 1 tiles ahead of its use.  Each buffer is
+  // its own LDS object and the tile loop is unrolled by NBUF, so the compiler
+  // can tell reads of one buffer from copies still landing in another (it
+  // would otherwise wait for every copy before the first LDS read).
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring depth");
+  __shared__ __attribute__((aligned(1024))) unsigned char sb0[2 * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb1[2 * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb2[NBUF > 2 ? 2 * T::kBytes : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb3[NBUF > 3 ? 2 * T::kBytes : 16];
+  auto ring = [&](int b) -> unsigned char* { return b == 0 ? sb0 : b == 1 ? sb1 : b == 2 ? sb2 : sb3; };
 
   const int lid = xcd_remap(blockIdx.x, total_wg);
   const int bh = lid / n_qtiles;
@@ -148,7 +157,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     ld_col[i] = 8 * c;
   }
   auto issue_tile_copy = [&](int kb, int buf) {
-    unsigned char* kt = smem + buf * 2 * T::kBytes;
+    unsigned char* kt = ring(buf);
     unsigned char* vt = kt + T::kBytes;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
@@ -184,49 +193,66 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   constexpr int kTStep = 16 * D * 2;  // 16 keys further: same swizzle phase
 
+  // Raw scores S^T of the current tile: sacc[nt][kh] holds keys 32kh..+31
+  // against query rows qw0 + 32nt + l32.
   f32x16 sacc[QT][2];
 
-  // S^T = K_j Q^T for the tile in LDS at kt, masked where needed.
-  auto scores = [&](const unsigned char* kt, int kb) {
+  // S^T for key half kh of the tile at kt, all query tiles (K reads shared).
+  auto scores_half = [&](const unsigned char* kt, int kh) {
 #pragma unroll
-    for (int nt = 0; nt < QT; ++nt) sacc[nt][0] = sacc[nt][1] = f32x16{};
+    for (int nt = 0; nt < QT; ++nt) sacc[nt][kh] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[ks] + kh * kKhStep);
 #pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[ks] + kh * kKhStep);
-#pragma unroll
-        for (int nt = 0; nt < QT; ++nt) sacc[nt][kh] = mfma32x32x16(a, qf[nt][ks], sacc[nt][kh]);
-      }
+      for (int nt = 0; nt < QT; ++nt) sacc[nt][kh] = mfma32x32x16(a, qf[nt][ks], sacc[nt][kh]);
     }
-    const bool need_mask = (kb + kBc > N) || (CAUSAL && kb + kBc - 1 > qw0);
-    if (need_mask) {
+  };
+
+  auto mask_half = [&](int kb, int kh) {
 #pragma unroll
-      for (int nt = 0; nt < QT; ++nt) {
-        const int qr = qw0 + nt * 32 + l32;
+    for (int nt = 0; nt < QT; ++nt) {
+      const int qr = qw0 + nt * 32 + l32;
 #pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb + 32 * kh + acc_row(i, g);
-            const bool vis = key < N && (!CAUSAL || key <= qr);
-            if (!vis) sacc[nt][kh][i] = kNegInf;
-          }
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int key = kb + 32 * kh + acc_row(i, g);
+        const bool vis = key < N && (!CAUSAL || key <= qr);
+        if (!vis) sacc[nt][kh][i] = kNegInf;
       }
     }
   };
 
-  // Exact running max of the raw scores of query tile nt: m moves up to it,
-  // U and l are rescaled by alpha = 2^(m_old - m_new) (0 while m_old = -inf).
-  auto exact_max_update = [&](int nt) {
-    float t8[8];
+  // P~ = 2^(s*c - m) for key half kh of query tile nt, rounded to bf16
+  // straight into the B operands pb[nt][2kh], pb[nt][2kh+1] of the second
+  // product (raw scores stay in sacc); rs[nt] gets the lane's fp32 partial
+  // sum.  Returns true when that sum is too large or m is not set yet.
+  float rs[QT];
+  bf16x8 pb[QT][4];
+  auto exponentials = [&](int nt, int kh) {
+    const float msafe = (m2[nt] == kNegInf) ? 0.f : m2[nt];
+    float r2[2];
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      t8[e] = fmaxf(fmaxf(sacc[nt][e >> 2][4 * (e & 3)], sacc[nt][e >> 2][4 * (e & 3) + 1]),
-                    fmaxf(sacc[nt][e >> 2][4 * (e & 3) + 2], sacc[nt][e >> 2][4 * (e & 3) + 3]));
-    float mx = fmaxf(fmaxf(fmaxf(t8[0], t8[1]), fmaxf(t8[2], t8[3])),
-                     fmaxf(fmaxf(t8[4], t8[5]), fmaxf(t8[6], t8[7])));
+    for (int th = 0; th < 2; ++th) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = fast_exp2(fmaf(sacc[nt][kh][8 * th + e], scale_log2, -msafe));
+      r2[th] = ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+      pb[nt][2 * kh + th] = pack_bf16x8(x);
+    }
+    rs[nt] = r2[0] + r2[1];
+    return !(rs[nt] <= kSumLimit) || m2[nt] == kNegInf;
+  };
+
+  // Slow path for key half kh of query tile nt: move m up to the exact
+  // running max (over the scores seen so far), rescale U and l by
+  // alpha = 2^(m_old - m_new) (0 while m_old = -inf), redo the exponentials.
+  auto rescue = [&](int nt, int kh) {
+    float t4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      t4[e] = fmaxf(fmaxf(sacc[nt][kh][4 * e], sacc[nt][kh][4 * e + 1]),
+                    fmaxf(sacc[nt][kh][4 * e + 2], sacc[nt][kh][4 * e + 3]));
+    float mx = fmaxf(fmaxf(t4[0], t4[1]), fmaxf(t4[2], t4[3]));
     mx = fmaxf(mx, shfl_xor_f32(mx, 32));
     const float mx2 = mx * scale_log2;
     const bool grow = mx2 > m2[nt];
@@ -235,70 +261,104 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     lsum[nt] *= alpha;
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt) oacc[nt][mt] *= alpha;
+    exponentials(nt, kh);
   };
 
-  // P~ = 2^(s*c - m) of query tile nt, rounded to bf16 straight into the B
-  // operands of the second product (the raw scores stay in sacc); rs gets the
-  // lane's fp32 partial row sum.  Returns whether that sum is too large.
-  float rs[QT];
-  bf16x8 pb[QT][4];
-  auto exponentials = [&](int nt) {
-    const float msafe = (m2[nt] == kNegInf) ? 0.f : m2[nt];
-    float r4[4];
+  // O^T += V^T P~^T for the 32 keys of half kh (V reads shared by the query tiles).
+  auto pv_half = [&](const unsigned char* vt, int kh) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float x[8];
+    for (int th = 0; th < 2; ++th) {
+      const int t = 2 * kh + th;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = fast_exp2(fmaf(sacc[nt][t >> 1][8 * (t & 1) + e], scale_log2, -msafe));
-      r4[t] = ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
-      pb[nt][t] = pack_bf16x8(x);
+      for (int mt = 0; mt < D / 32; ++mt) {
+        const u32x2 lo = lds_read_tr16(vt + voff[0][mt] + t * kTStep);
+        const u32x2 hi = lds_read_tr16(vt + voff[1][mt] + t * kTStep);
+        const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+        const bf16x8 a = bitcast<bf16x8>(w);
+#pragma unroll
+        for (int nt = 0; nt < QT; ++nt) oacc[nt][mt] = mfma32x32x16(a, pb[nt][t], oacc[nt][mt]);
+      }
     }
-    rs[nt] = (r4[0] + r4[1]) + (r4[2] + r4[3]);
-    return !(rs[nt] <= kSumLimit);
   };
 
-  if (nblk > 0) issue_tile_copy(0, 0);
-  wait_all_memory();
-  __syncthreads();
+  // Instruction interleave for a step that overlaps MFMAs with the
+  // exponentials of the other key half: per MFMA, its LDS operand reads and
+  // an equal share of the vector ALU work.
+  constexpr int kStepMfma = (D / 16) * QT;          // = 2 * (D / 32) * QT
+  constexpr int kValuPerMfma = (56 * QT) / kStepMfma;
 
-  for (int j = 0; j < nblk; ++j) {
+  // One wave-uniform branch for all query tiles, so that every exponential
+  // of the step is needed before it (and stays in the step's block).
+  auto check_half = [&](int kh) {
+    bool bad = false;
+#pragma unroll
+    for (int nt = 0; nt < QT; ++nt) bad |= !(rs[nt] <= kSumLimit) || m2[nt] == kNegInf;
+    if (__ballot(bad)) {
+#pragma unroll
+      for (int nt = 0; nt < QT; ++nt)
+        if (__ballot(!(rs[nt] <= kSumLimit) || m2[nt] == kNegInf)) rescue(nt, kh);
+    }
+#pragma unroll
+    for (int nt = 0; nt < QT; ++nt) lsum[nt] += rs[nt];
+  };
+
+#pragma unroll
+  for (int p = 0; p < NBUF - 1; ++p)
+    if (p < nblk) issue_tile_copy(p * kBc, p);
+
+  for (int j0 = 0; j0 < nblk; j0 += NBUF) {
+#pragma unroll
+  for (int u = 0; u < NBUF; ++u) {
+    const int j = j0 + u;
+    if (j >= nblk) break;
     const int kb = j * kBc;
-    const int buf = j & 1;
-    if (j + 1 < nblk) issue_tile_copy(kb + kBc, buf ^ 1);
-    const unsigned char* kt = smem + buf * 2 * T::kBytes;
+    // Tile j's copies are done when at most the copies of the NBUF - 2
+    // tiles after it are still in flight (2 * NLD per tile and wavefront);
+    // the barrier then makes every wavefront's part visible and guarantees
+    // that nobody still reads the buffer the next copy overwrites.
+    if (j + NBUF - 2 < nblk) {
+      wait_vm_at_most<(NBUF - 2) * 2 * NLD>();
+    } else {
+      wait_vm_at_most<0>();
+    }
+    lds_barrier();
+    if (j + NBUF - 1 < nblk) issue_tile_copy(kb + (NBUF - 1) * kBc, (u + NBUF - 1) % NBUF);
+    const unsigned char* kt = ring(u);
     const unsigned char* vt = kt + T::kBytes;
 
     const bool active = !CAUSAL || kb <= qw0 + 32 * QT - 1;
     if (active) {
-      scores(kt, kb);
+      const bool need_mask = (kb + kBc > N) || (CAUSAL && kb + kBc - 1 > qw0);
+      // step 0: scores of key half 0
+      scores_half(kt, 0);
+      if (need_mask) mask_half(kb, 0);
+      // step 1: scores of key half 1 | exponentials of key half 0
+      scores_half(kt, 1);
 #pragma unroll
-      for (int nt = 0; nt < QT; ++nt) {
-        if (j == 0) exact_max_update(nt);
-        if (__ballot(exponentials(nt))) {
-          // rare: the reference fell too far below this tile's scores
-          exact_max_update(nt);
-          exponentials(nt);
-        }
-        lsum[nt] += rs[nt];
+      for (int nt = 0; nt < QT; ++nt) exponentials(nt, 0);
+#pragma unroll
+      for (int i = 0; i < kStepMfma; ++i) {
+        if (i < D / 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
       }
-
-      // O^T += V_j^T P~^T
+      check_half(0);
+      if (need_mask) mask_half(kb, 1);
+      // step 2: P~V of key half 0 | exponentials of key half 1
+      pv_half(vt, 0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int nt = 0; nt < QT; ++nt) exponentials(nt, 1);
 #pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt) {
-          const u32x2 lo = lds_read_tr16(vt + voff[0][mt] + t * kTStep);
-          const u32x2 hi = lds_read_tr16(vt + voff[1][mt] + t * kTStep);
-          const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-          const bf16x8 a = bitcast<bf16x8>(w);
-#pragma unroll
-          for (int nt = 0; nt < QT; ++nt) oacc[nt][mt] = mfma32x32x16(a, pb[nt][t], oacc[nt][mt]);
-        }
+      for (int i = 0; i < kStepMfma; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x100, (D / 8) / kStepMfma > 0 ? (D / 8) / kStepMfma : 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kValuPerMfma, 0);
       }
+      check_half(1);
+      // step 3: P~V of key half 1
+      pv_half(vt, 1);
     }
-
-    wait_all_memory();
-    __syncthreads();
+  }
   }
 
   // Epilogue: O = U / l (bf16, RNE) and LSE = (m + log2 l) * ln 2.
@@ -476,13 +536,13 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
   }
 }
 
-template <int D, int QT, bool CAUSAL>
+template <int D, int QT, int NBUF, bool CAUSAL>
 hipError_t run_bf16(const FwdArgs& a, hipStream_t s) {
   constexpr int BR = kWaves * 32 * QT;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const int total = n_qtiles * a.B * a.H;
   const float scale_log2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, CAUSAL>), dim3(total), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NBUF, CAUSAL>), dim3(total), dim3(kThreads), 0, s,
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                      static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse, a.N, n_qtiles,
                      total, scale_log2);
@@ -504,8 +564,8 @@ hipError_t run_f32(const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
-  if (a.d == 64) return a.causal ? run_bf16<64, 2, true>(a, s) : run_bf16<64, 2, false>(a, s);
-  return a.causal ? run_bf16<128, 1, true>(a, s) : run_bf16<128, 1, false>(a, s);
+  if (a.d == 64) return a.causal ? run_bf16<64, 2, 4, true>(a, s) : run_bf16<64, 2, 4, false>(a, s);
+  return a.causal ? run_bf16<128, 1, 2, true>(a, s) : run_bf16<128, 1, 2, false>(a, s);
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {
