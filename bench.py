@@ -120,7 +120,15 @@ def main():
     ap.add_argument("--no-long", action="store_true", help="skip the reported-only long causal forward")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--only", default="",
+                    help="comma-separated subset of fwd,decode,bwd,fwd_long to run (profiling passes)")
     a = ap.parse_args()
+    parts = ["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long"])
+    if a.only:
+        parts = [p for p in a.only.split(",") if p]
+        bad = [p for p in parts if p not in ("fwd", "decode", "bwd", "fwd_long")]
+        if bad:
+            ap.error(f"unknown --only parts {bad}")
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(the per-(b, h) work would shard over GPUs with no communication).", file=sys.stderr)
@@ -140,23 +148,27 @@ def main():
         return [make_tensor(seed, n, B, H, N, d, bf16, scale, device=dev) for n in names]
 
     print("bench: generating inputs", file=sys.stderr, flush=True)
-    c = FWD
-    fq, fk, fv = mk(0, ("q", "k", "v"), c["B"], c["H"], c["N"], c["d"])
-    fo = torch.empty_like(fq)
-    flse = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device=dev)
-    c = DEC
-    dq_ = make_tensor(0, "q", c["B"], c["H"], 1, c["d"], bf16, device=dev)
-    dk_, dv_ = mk(0, ("k", "v"), c["B"], c["H"], c["L"], c["d"])
-    do_ = torch.empty_like(dq_)
-    dlse = torch.empty((c["B"], c["H"]), dtype=torch.float32, device=dev)
-    dws = torch.empty(attn_decode_workspace_bytes(c["B"], c["H"], c["d"], c["S"]) // 4, dtype=torch.float32,
-                      device=dev)
-    c = BWD
-    bq, bk, bv, bdo = mk(0, ("q", "k", "v", "do"), c["B"], c["H"], c["N"], c["d"])
-    bo, blse = attn_fwd(bq, bk, bv, causal=True)
-    bgq, bgk, bgv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
-    bws = torch.empty(attn_bwd_workspace_bytes(c["B"], c["H"], c["N"]) // 4, dtype=torch.float32, device=dev)
-    if not a.no_long:
+    if "fwd" in parts:
+        c = FWD
+        fq, fk, fv = mk(0, ("q", "k", "v"), c["B"], c["H"], c["N"], c["d"])
+        fo = torch.empty_like(fq)
+        flse = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device=dev)
+    if "decode" in parts:
+        c = DEC
+        dq_ = make_tensor(0, "q", c["B"], c["H"], 1, c["d"], bf16, device=dev)
+        dk_, dv_ = mk(0, ("k", "v"), c["B"], c["H"], c["L"], c["d"])
+        do_ = torch.empty_like(dq_)
+        dlse = torch.empty((c["B"], c["H"]), dtype=torch.float32, device=dev)
+        dws = torch.empty(attn_decode_workspace_bytes(c["B"], c["H"], c["d"], c["S"]) // 4,
+                          dtype=torch.float32, device=dev)
+    if "bwd" in parts:
+        c = BWD
+        bq, bk, bv, bdo = mk(0, ("q", "k", "v", "do"), c["B"], c["H"], c["N"], c["d"])
+        bo, blse = attn_fwd(bq, bk, bv, causal=True)
+        bgq, bgk, bgv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
+        bws = torch.empty(attn_bwd_workspace_bytes(c["B"], c["H"], c["N"]) // 4, dtype=torch.float32,
+                          device=dev)
+    if "fwd_long" in parts:
         c = FWD_LONG
         lq, lk, lv = mk(0, ("q", "k", "v"), c["B"], c["H"], c["N"], c["d"], c["input_scale"])
         lo = torch.empty_like(lq)
@@ -172,19 +184,22 @@ def main():
         del src, dst
 
     stream = torch.cuda.current_stream(dev)
-    names = ["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long"])
+    names = parts
 
     def step(ev):
-        ev["fwd"][0].record(stream)
-        attn_fwd(fq, fk, fv, causal=False, out=fo, lse=flse)
-        ev["fwd"][1].record(stream)
-        ev["decode"][0].record(stream)
-        attn_fwd_splitk_decode(dq_, dk_, dv_, DEC["S"], out=do_, lse=dlse, workspace=dws)
-        ev["decode"][1].record(stream)
-        ev["bwd"][0].record(stream)
-        attn_bwd(bq, bk, bv, bo, bdo, blse, causal=True, dq=bgq, dk=bgk, dv=bgv, workspace=bws)
-        ev["bwd"][1].record(stream)
-        if not a.no_long:
+        if "fwd" in names:
+            ev["fwd"][0].record(stream)
+            attn_fwd(fq, fk, fv, causal=False, out=fo, lse=flse)
+            ev["fwd"][1].record(stream)
+        if "decode" in names:
+            ev["decode"][0].record(stream)
+            attn_fwd_splitk_decode(dq_, dk_, dv_, DEC["S"], out=do_, lse=dlse, workspace=dws)
+            ev["decode"][1].record(stream)
+        if "bwd" in names:
+            ev["bwd"][0].record(stream)
+            attn_bwd(bq, bk, bv, bo, bdo, blse, causal=True, dq=bgq, dk=bgk, dv=bgv, workspace=bws)
+            ev["bwd"][1].record(stream)
+        if "fwd_long" in names:
             ev["fwd_long"][0].record(stream)
             attn_fwd(lq, lk, lv, causal=True, out=lo, lse=llse)
             ev["fwd_long"][1].record(stream)
@@ -208,12 +223,18 @@ def main():
     total_ms = t0.elapsed_time(t1)
     ms = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in evs) / a.steps for n in names}
 
-    fwd_tf = fwd_flops(FWD) / (ms["fwd"] * 1e-3) / 1e12
-    dec_gbps = dec_bytes(DEC) / (ms["decode"] * 1e-3) / 1e9
-    bwd_tf = 2.5 * fwd_flops(BWD) / (ms["bwd"] * 1e-3) / 1e12
+    def rate(name, work, unit_div):
+        return work / (ms[name] * 1e-3) / unit_div if name in ms else None
+
+    def rnd(x, n):
+        return None if x is None else round(x, n)
+
+    fwd_tf = rate("fwd", fwd_flops(FWD), 1e12)
+    dec_gbps = rate("decode", dec_bytes(DEC), 1e9)
+    bwd_tf = rate("bwd", 2.5 * fwd_flops(BWD), 1e12)
     out = {
         "metric": METRIC,
-        "value": round(fwd_tf, 3),
+        "value": rnd(fwd_tf, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": a.steps,
@@ -231,36 +252,42 @@ def main():
             "global_batch": FWD["B"],
             "seq_len": FWD["N"],
             "parallelism": "single GPU",
+            "parts": names,
         },
-        "fwd_pct_bf16_peak": round(100.0 * fwd_tf / PEAK_BF16_TFLOPS, 2),
-        "fwd_us": round(ms["fwd"] * 1e3, 2),
-        "decode_gbps": round(dec_gbps, 1),
-        "decode_pct_hbm": round(100.0 * dec_gbps / PEAK_HBM_GBPS, 2),
-        "decode_us": round(ms["decode"] * 1e3, 2),
-        "bwd_tflops": round(bwd_tf, 3),
-        "bwd_us": round(ms["bwd"] * 1e3, 2),
-        "roofline": {
+    }
+    if fwd_tf is not None:
+        out["fwd_pct_bf16_peak"] = round(100.0 * fwd_tf / PEAK_BF16_TFLOPS, 2)
+        out["fwd_us"] = round(ms["fwd"] * 1e3, 2)
+    if dec_gbps is not None:
+        out["decode_gbps"] = round(dec_gbps, 1)
+        out["decode_pct_hbm"] = round(100.0 * dec_gbps / PEAK_HBM_GBPS, 2)
+        out["decode_us"] = round(ms["decode"] * 1e3, 2)
+    if bwd_tf is not None:
+        out["bwd_tflops"] = round(bwd_tf, 3)
+        out["bwd_us"] = round(ms["bwd"] * 1e3, 2)
+    if fwd_tf is not None:
+        out["roofline"] = {
             "bound": "mfma",
             "achieved": round(fwd_tf, 3),
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(fwd_tf / PEAK_BF16_TFLOPS, 4),
             "traffic": _traffic("fwd_bf16_d64", ["fwd.hip", "common.h"]),
-        },
-        "roofline_decode": {
+        }
+    if dec_gbps is not None:
+        out["roofline_decode"] = {
             "bound": "hbm",
             "achieved": round(dec_gbps, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
             "traffic": _traffic("decode_d128", ["decode.hip", "common.h"]),
-        },
-    }
-    if not a.no_long:
+        }
+    if "fwd_long" in ms:
         lt = fwd_flops(FWD_LONG) / (ms["fwd_long"] * 1e-3) / 1e12
         out["fwd_long_causal_tflops"] = round(lt, 3)
         out["fwd_long_causal_us"] = round(ms["fwd_long"] * 1e3, 2)
-    if not a.no_cpu_baseline:
+    if not a.no_cpu_baseline and "fwd" in names:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out), flush=True)

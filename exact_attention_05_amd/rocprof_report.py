@@ -1,0 +1,234 @@
+"""Summaries of rocprofv3 output for the attention kernels.
+
+Turns the CSV files that ``rocprofv3 --kernel-trace --stats`` and
+``rocprofv3 --pmc ...`` write into short Markdown tables, and derives
+
+* per-kernel achieved TFLOP/s or GB/s against MI355X's peaks, from the
+  algorithmic work per launch and the kernel's average duration;
+* HBM traffic per launch from ``FETCH_SIZE`` / ``WRITE_SIZE`` (KiB per
+  dispatch), each scaled by what the same counter reads for a plain device
+  copy of known size in the same run;
+* instruction mix (VALU, transcendental, MFMA, LDS) from the SQ counters.
+
+Only parsing happens here; the profiler itself runs as its own command with
+the program after ``--``.  Usage::
+
+    python -m exact_attention_05_amd.rocprof_report stats DIR --title T --cmd C
+    python -m exact_attention_05_amd.rocprof_report traffic --fetch DIR --write DIR \
+        --kernel REGEX --calib-mib 256 --key NAME --sources fwd.hip,common.h --cmd C
+    python -m exact_attention_05_amd.rocprof_report counters DIR --kernel REGEX
+"""
+
+import argparse
+import collections
+import csv
+import glob
+import hashlib
+import json
+import os
+import re
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+
+PEAK_BF16_TFLOPS = 2516.6
+PEAK_HBM_GBPS = 8000.0
+COPY_KERNEL = r"copyBuffer"
+
+
+def short_name(n):
+    """Readable name of a mangled attention kernel (template arguments kept)."""
+    n = n.replace("_ZN4attn12_GLOBAL__N_1", "")
+    m = re.match(r"(\d+)", n)
+    if m:
+        ln = int(m.group(1))
+        start = len(m.group(1))
+        base = n[start:start + ln]
+        rest = n[start + ln:]
+        args = [a or ("true" if b == "1" else "false") for a, b in re.findall(r"Li(\d+)E|Lb(\d)E", rest)]
+        return f"{base}<{','.join(args)}>" if args else base
+    n = n.replace("(anonymous namespace)::", "").split("(")[0]
+    return re.sub(r"^void |attn::", "", n)
+
+
+def _find(d, suffix):
+    hits = sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True))
+    if not hits:
+        raise FileNotFoundError(f"no *{suffix} under {d}")
+    return hits[0]
+
+
+def kernel_stats(d):
+    """[(name, calls, avg_ns, min_ns, max_ns, pct)] from the --stats CSV."""
+    rows = []
+    with open(_find(d, "kernel_stats.csv")) as f:
+        for r in csv.DictReader(f):
+            rows.append((r["Name"], int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                         float(r["MaxNs"]), float(r["Percentage"])))
+    return rows
+
+
+def counter_values(d):
+    """{(kernel_name, counter): [value per dispatch]} from a --pmc run."""
+    out = collections.defaultdict(list)
+    with open(_find(d, "counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            out[(r["Kernel_Name"], r["Counter_Name"])].append(float(r["Counter_Value"]))
+    return out
+
+
+def _match(vals, kernel_re, counter):
+    hits = [v for (k, c), v in vals.items() if c == counter and re.search(kernel_re, k)]
+    if not hits:
+        raise KeyError(f"no {counter} values for kernels matching {kernel_re!r}")
+    flat = [x for h in hits for x in h]
+    return sum(flat) / len(flat), len(flat)
+
+
+def _largest(vals, kernel_re, counter):
+    hits = [x for (k, c), v in vals.items() if c == counter and re.search(kernel_re, k) for x in v]
+    if not hits:
+        raise KeyError(f"no {counter} values for kernels matching {kernel_re!r}")
+    return max(hits)
+
+
+def src_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def cmd_stats(a):
+    rows = kernel_stats(a.dir)
+    work = {}
+    for spec in a.work or []:
+        # REGEX=AMOUNT:UNIT with UNIT in {flop, byte}
+        rx, rest = spec.rsplit("=", 1)
+        amt, unit = rest.split(":")
+        work[rx] = (float(amt), unit)
+    lines = [f"# {a.title}", "", "Command (GPU box, repo root):", "", "```", a.cmd, "```", ""]
+    lines.append("| kernel | calls | average (us) | min (us) | max (us) | share | achieved vs peak |")
+    lines.append("|---|---|---|---|---|---|---|")
+    for name, calls, avg, mn, mx, pct in rows:
+        ach = ""
+        for rx, (amt, unit) in work.items():
+            if re.search(rx, name):
+                if unit == "flop":
+                    t = amt / (avg * 1e-9) / 1e12
+                    ach = f"{t:.1f} TFLOP/s = {100 * t / PEAK_BF16_TFLOPS:.1f}% of bf16 MFMA"
+                else:
+                    g = amt / (avg * 1e-9) / 1e9
+                    ach = f"{g:.1f} GB/s = {100 * g / PEAK_HBM_GBPS:.1f}% of HBM"
+        lines.append(f"| `{short_name(name)}` | {calls} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | "
+                     f"{pct:.1f}% | {ach} |")
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def cmd_traffic(a):
+    fv = counter_values(a.fetch)
+    wv = counter_values(a.write)
+    calib = a.calib_mib * 2 ** 20
+    # the calibration copy is the largest copy dispatch of the run (input
+    # uploads may add small ones)
+    f_copy = _largest(fv, COPY_KERNEL, "FETCH_SIZE")
+    w_copy = _largest(wv, COPY_KERNEL, "WRITE_SIZE")
+    f_scale = calib / (f_copy * 1024.0)
+    w_scale = calib / (w_copy * 1024.0)
+    f_k, nf = _match(fv, a.kernel, "FETCH_SIZE")
+    w_k, nw = _match(wv, a.kernel, "WRITE_SIZE")
+    fetch_b = f_k * 1024.0 * f_scale
+    write_b = w_k * 1024.0 * w_scale
+    total = fetch_b + write_b
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    tab = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            tab = json.load(f)
+    srcs = a.sources.split(",")
+    tab[a.key] = {
+        "bytes_per_launch": round(total),
+        "fetch_bytes": round(fetch_b),
+        "write_bytes": round(write_b),
+        "fetch_scale": round(f_scale, 4),
+        "write_scale": round(w_scale, 4),
+        "kernel_regex": a.kernel,
+        "sources": srcs,
+        "source_sha": src_sha(srcs),
+    }
+    with open(path, "w") as f:
+        json.dump(tab, f, indent=1, sort_keys=True)
+        f.write("\n")
+    lines = [
+        f"# HBM traffic of `{a.kernel}` ({a.key})", "", "Commands (GPU box, repo root):", "", "```", a.cmd, "```", "",
+        f"Calibration: a device copy of {a.calib_mib} MiB reads FETCH_SIZE = {f_copy:.1f} KiB and "
+        f"WRITE_SIZE = {w_copy:.1f} KiB, so the counters are scaled by {f_scale:.4f} (fetch) and "
+        f"{w_scale:.4f} (write).", "",
+        "| counter | raw KiB per dispatch | dispatches | scaled bytes per launch |",
+        "|---|---|---|---|",
+        f"| FETCH_SIZE | {f_k:.1f} | {nf} | {fetch_b:.0f} |",
+        f"| WRITE_SIZE | {w_k:.1f} | {nw} | {write_b:.0f} |",
+        f"| total | | | {total:.0f} |",
+    ]
+    if a.algorithmic:
+        lines.append("")
+        lines.append(f"Algorithmic bytes per launch: {a.algorithmic:.0f}; measured / algorithmic = "
+                     f"{total / a.algorithmic:.3f}.")
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def cmd_counters(a):
+    vals = counter_values(a.dir)
+    names = sorted({c for (k, c) in vals if re.search(a.kernel, k)})
+    print(f"| counter | mean per dispatch |\n|---|---|")
+    got = {}
+    for c in names:
+        v, _ = _match(vals, a.kernel, c)
+        got[c] = v
+        print(f"| {c} | {v:.1f} |")
+    if "SQ_INSTS_MFMA" in got and "SQ_INSTS_VALU" in got:
+        print(f"\nVALU instructions per MFMA instruction: {got['SQ_INSTS_VALU'] / got['SQ_INSTS_MFMA']:.2f}")
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("dir")
+    s.add_argument("--title", required=True)
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out")
+    s.add_argument("--work", action="append", help="REGEX=AMOUNT:flop|byte per launch")
+    s.set_defaults(fn=cmd_stats)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--calib-mib", type=int, required=True)
+    t.add_argument("--key", required=True)
+    t.add_argument("--sources", required=True)
+    t.add_argument("--cmd", required=True)
+    t.add_argument("--algorithmic", type=float, default=0.0)
+    t.add_argument("--out")
+    t.set_defaults(fn=cmd_traffic)
+    c = sub.add_parser("counters")
+    c.add_argument("dir")
+    c.add_argument("--kernel", required=True)
+    c.set_defaults(fn=cmd_counters)
+    a = ap.parse_args(argv)
+    a.fn(a)
+
+
+if __name__ == "__main__":
+    sys.exit(main())
