@@ -385,6 +385,307 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // ---------------------------------------------------------------------------
+// Ping-pong variant.  Eight wavefronts, two per SIMD: wavefronts 0-3 lead and
+// 4-7 trail by one phase.  Per K/V tile j a wavefront runs a matrix phase
+// (S_j^T = K_j Q^T for the whole tile, then O^T += V_{j-1}^T P~_{j-1}^T) and
+// a vector phase (mask, exponentials P~_j, row sums, reference check).  A
+// workgroup barrier separates phases, so on every SIMD one wavefront issues
+// matrix instructions while the other does the exponentials of its own tile,
+// instead of both competing for the same unit.  The matrix-phase wavefront
+// runs at raised issue priority so that its next product starts as soon as
+// the matrix unit frees up.  Online state, reference rules and LDS layout
+// are those of fwd_bf16_kernel; tile t's K is read in phases 2t and 2t+1,
+// its V in phases 2t+2 and 2t+3, and tile t+2 is copied at phase 2t.
+// ---------------------------------------------------------------------------
+template <int D, int QT, bool CAUSAL>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void fwd_pp_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    __bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg,
+    float scale_log2) {
+  using T = TileLayout<D>;
+  constexpr int NW = 8;
+  constexpr int BR = NW * 32 * QT;
+  constexpr int NCP = 2 * (D / 8) / NW;  // 1 KB copies per wavefront per tile
+  static_assert(NCP >= 1 && NCP * NW == 2 * (D / 8), "tile copy split");
+  __shared__ __attribute__((aligned(1024))) unsigned char sb0[2 * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb1[2 * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb2[2 * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb3[2 * T::kBytes];
+
+  const int lid = xcd_remap(blockIdx.x, total_wg);
+  const int bh = lid / n_qtiles;
+  int qtile = lid % n_qtiles;
+  if (CAUSAL) qtile = n_qtiles - 1 - qtile;  // longest rows first
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const bool lead = wave < 4;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int64_t base = (int64_t)bh * N * D;
+  const __bf16* Qh = Q + base;
+  const __bf16* Kh = K + base;
+  const __bf16* Vh = V + base;
+  __bf16* Oh = O + base;
+
+  const int q0 = qtile * BR;
+  const int qw0 = q0 + wave * 32 * QT;
+  const int kend = CAUSAL ? min(N, q0 + BR) : N;
+  const int ntiles = (kend + kBc - 1) / kBc;
+
+  int ld_key[NCP], ld_col[NCP], ld_dst[NCP];
+  bool ld_v[NCP];
+#pragma unroll
+  for (int i = 0; i < NCP; ++i) {
+    const int c = wave * NCP + i;
+    const int cl = c % (D / 8);
+    const int line = 4 * cl + (lane >> 4);
+    int k, ch;
+    T::at(line, lane & 15, k, ch);
+    ld_key[i] = k;
+    ld_col[i] = 8 * ch;
+    ld_v[i] = c >= D / 8;
+    ld_dst[i] = (ld_v[i] ? T::kBytes : 0) + 4 * cl * 256;
+  }
+  auto issue_tile_copy = [&](int kb, unsigned char* kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NCP; ++i) {
+      const int row = min(kb + ld_key[i], N - 1);  // rows past the end are masked out
+      const int64_t off = (int64_t)row * D + ld_col[i];
+      global_to_lds16((ld_v[i] ? Vh : Kh) + off, kt + ld_dst[i]);
+    }
+  };
+
+  issue_tile_copy(0, sb0);
+  if (ntiles > 1) issue_tile_copy(kBc, sb1);
+
+  bf16x8 qf[QT][D / 16];
+#pragma unroll
+  for (int nt = 0; nt < QT; ++nt) {
+    const int qr = qw0 + nt * 32 + l32;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      qf[nt][ks] = qr < N ? *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
+  }
+
+  f32x16 oacc[QT][D / 32];
+  float m2[QT], lsum[QT], rs[QT];
+#pragma unroll
+  for (int nt = 0; nt < QT; ++nt) {
+    m2[nt] = kNegInf;
+    lsum[nt] = 0.f;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt) oacc[nt][mt] = f32x16{};
+  }
+
+  int koff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = T::offset(l32, 2 * ks + g);
+  constexpr int kKhStep = 32 * D * 2;
+  int voff[2][D / 32];
+  {
+    const int s = lane & 15, G = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) {
+        const int key = 8 * h + 4 * (G >> 1) + (s >> 2);
+        const int dim = 32 * mt + 16 * (G & 1) + 4 * (s & 3);
+        voff[h][mt] = T::offset(key, dim >> 3) + 8 * ((dim >> 2) & 1);
+      }
+  }
+  constexpr int kTStep = 16 * D * 2;
+
+  f32x16 sacc[QT][2];  // S^T of the current tile, two halves of 32 keys
+  bf16x8 pb[QT][4];    // P~ of the previous tile, four 16-key operands
+
+  // S^T = K Q^T for the tile whose K is at kt (both halves).
+  auto scores = [&](const unsigned char* kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int nt = 0; nt < QT; ++nt) sacc[nt][0] = sacc[nt][1] = f32x16{};
+    bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[0]);
+#pragma unroll
+    for (int r = 0; r < 2 * (D / 16); ++r) {
+      const int hh = r / (D / 16), ks = r % (D / 16);
+      bf16x8 an = a;
+      if (r + 1 < 2 * (D / 16)) {
+        const int hn = (r + 1) / (D / 16), kn = (r + 1) % (D / 16);
+        an = *reinterpret_cast<const bf16x8*>(kt + koff[kn] + hn * kKhStep);
+      }
+#pragma unroll
+      for (int nt = 0; nt < QT; ++nt) sacc[nt][hh] = mfma32x32x16(a, qf[nt][ks], sacc[nt][hh]);
+      a = an;
+    }
+  };
+  // V^T operand of 16-key slice t, dims 32mt..+31 (two transposing reads).
+  auto vop = [&](const unsigned char* vt, int t, int mt) __attribute__((always_inline)) {
+    const u32x2 lo = lds_read_tr16(vt + voff[0][mt] + t * kTStep);
+    const u32x2 hi = lds_read_tr16(vt + voff[1][mt] + t * kTStep);
+    const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+    return bitcast<bf16x8>(w);
+  };
+  // Matrix phase of tile j: O^T += V_{j-1}^T P~_{j-1}^T (V at vt) first, so
+  // that P~ dies before S_j^T = K_j Q^T (K at kt) is written; either part may
+  // be absent (first and last phases).  Each operand is read one product
+  // ahead of its use, so LDS latency overlaps the matrix unit.
+  auto mphase = [&](const unsigned char* kt, const unsigned char* vt, bool do_pv, bool do_qk)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    if (do_pv) {
+      bf16x8 a = vop(vt, 0, 0);
+#pragma unroll
+      for (int r = 0; r < 4 * (D / 32); ++r) {
+        const int t = r / (D / 32), mt = r % (D / 32);
+        bf16x8 an = a;
+        if (r + 1 < 4 * (D / 32)) an = vop(vt, (r + 1) / (D / 32), (r + 1) % (D / 32));
+#pragma unroll
+        for (int nt = 0; nt < QT; ++nt) oacc[nt][mt] = mfma32x32x16(a, pb[nt][t], oacc[nt][mt]);
+        a = an;
+      }
+    }
+    if (do_qk) scores(kt);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // P~ = 2^(s*c - m) of query tile nt, rounded to bf16; rs = lane's fp32 sum.
+  auto expo = [&](int nt) __attribute__((always_inline)) {
+    float r4[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = fast_exp2(fmaf(sacc[nt][t >> 1][8 * (t & 1) + e], scale_log2, -m2[nt]));
+      r4[t] = ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+      pb[nt][t] = pack_bf16x8(x);
+    }
+    rs[nt] = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+  };
+
+  auto mask_tile = [&](int j) __attribute__((always_inline)) {
+    const int kb = j * kBc;
+    if ((kb + kBc > N) || (CAUSAL && kb + kBc - 1 > qw0)) {
+#pragma unroll
+      for (int nt = 0; nt < QT; ++nt) {
+        const int qr = qw0 + nt * 32 + l32;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb + 32 * hh + acc_row(i, g);
+            const bool vis = key < N && (!CAUSAL || key <= qr);
+            if (!vis) sacc[nt][hh][i] = kNegInf;
+          }
+      }
+    }
+  };
+  auto row_max2 = [&](int nt) __attribute__((always_inline)) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[nt][0][i], sacc[nt][1][i]));
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    return mx * scale_log2;
+  };
+
+  // Vector phase of tile j (K still in LDS at kt).  The scores die as the
+  // exponentials are formed; the rare rescue recomputes them from K.
+  auto vphase = [&](int j, const unsigned char* kt) __attribute__((always_inline)) {
+    mask_tile(j);
+    if (j == 0) {
+      // the reference m: exact row max of tile 0 (key 0 is visible to every row)
+#pragma unroll
+      for (int nt = 0; nt < QT; ++nt) m2[nt] = row_max2(nt);
+    }
+#pragma unroll
+    for (int nt = 0; nt < QT; ++nt) expo(nt);
+    bool bad = false;
+#pragma unroll
+    for (int nt = 0; nt < QT; ++nt) bad |= !(rs[nt] <= kSumLimit);
+    if (__builtin_expect(__ballot(bad) != 0, 0)) {
+      __builtin_amdgcn_sched_barrier(0);
+      scores(kt);
+      mask_tile(j);
+#pragma unroll
+      for (int nt = 0; nt < QT; ++nt) {
+        const float mx2 = row_max2(nt);
+        const bool grow = mx2 > m2[nt];
+        const float alpha = grow ? fast_exp2(m2[nt] - mx2) : 1.f;
+        m2[nt] = grow ? mx2 : m2[nt];
+        lsum[nt] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) oacc[nt][mt] *= alpha;
+        expo(nt);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int nt = 0; nt < QT; ++nt) lsum[nt] += rs[nt];
+  };
+
+  auto phase_barrier = [&]() __attribute__((always_inline)) { lds_barrier(); };
+
+  // One tile step = two phases.  kt: tile j's buffer, vprev: tile j-1's
+  // buffer, next: where tile j+2 goes.
+  auto tile_step = [&](int j, unsigned char* kt, unsigned char* vprev, unsigned char* next)
+      __attribute__((always_inline)) {
+    if (j + 1 < ntiles) wait_vm_at_most<NCP>(); else wait_vm_at_most<0>();
+    phase_barrier();
+    if (j + 2 < ntiles) issue_tile_copy((j + 2) * kBc, next);
+    const unsigned char* vt = vprev + T::kBytes;
+    if (lead) mphase(kt, vt, true, true);
+    else vphase(j - 1, vprev);
+    phase_barrier();
+    if (lead) vphase(j, kt);
+    else mphase(kt, vt, true, true);
+  };
+
+  // Tile 0: scores only.
+  if (ntiles > 1) wait_vm_at_most<NCP>(); else wait_vm_at_most<0>();
+  phase_barrier();
+  if (ntiles > 2) issue_tile_copy(2 * kBc, sb2);
+  if (lead) mphase(sb0, nullptr, false, true);
+  phase_barrier();
+  if (lead) vphase(0, sb0);
+  else mphase(sb0, nullptr, false, true);
+  for (int j = 1; j < ntiles; j += 4) {
+    tile_step(j, sb1, sb0, sb3);
+    if (j + 1 < ntiles) tile_step(j + 1, sb2, sb1, sb0); else break;
+    if (j + 2 < ntiles) tile_step(j + 2, sb3, sb2, sb1); else break;
+    if (j + 3 < ntiles) tile_step(j + 3, sb0, sb3, sb2); else break;
+  }
+  // Final phases: products of the last tile (ring slot (ntiles - 1) % 4).
+  {
+    const int tl = ntiles - 1;
+    const unsigned char* kt = (tl & 3) == 0 ? sb0 : (tl & 3) == 1 ? sb1 : (tl & 3) == 2 ? sb2 : sb3;
+    const unsigned char* vt = kt + T::kBytes;
+    phase_barrier();
+    if (lead) mphase(nullptr, vt, true, false);
+    else vphase(tl, kt);
+    phase_barrier();
+    if (!lead) mphase(nullptr, vt, true, false);
+  }
+
+#pragma unroll
+  for (int nt = 0; nt < QT; ++nt) {
+    const int qr = qw0 + nt * 32 + l32;
+    const float lt = lsum[nt] + shfl_xor_f32(lsum[nt], 32);
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    if (qr < N) {
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int d0 = 32 * mt + 8 * c + 4 * g;
+          u32x2 w = {pack_bf16x2(oacc[nt][mt][4 * c] * inv, oacc[nt][mt][4 * c + 1] * inv),
+                     pack_bf16x2(oacc[nt][mt][4 * c + 2] * inv, oacc[nt][mt][4 * c + 3] * inv)};
+          *reinterpret_cast<u32x2*>(Oh + (int64_t)qr * D + d0) = w;
+        }
+      }
+      if (g == 0 && LSE != nullptr)
+        LSE[(int64_t)bh * N + qr] = lt > 0.f ? (m2[nt] + fast_log2(lt)) * kLn2 : kNegInf;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 inputs, d = 64: same loop with v_mfma_f32_32x32x2_f32; P~ stays fp32
 // and V needs no transpose (one fp32 per lane per MFMA operand).
 // ---------------------------------------------------------------------------
@@ -549,6 +850,18 @@ hipError_t run_bf16(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int D, int QT, bool CAUSAL>
+hipError_t run_pp(const FwdArgs& a, hipStream_t s) {
+  constexpr int BR = 8 * 32 * QT;
+  const int n_qtiles = (a.N + BR - 1) / BR;
+  const int total = n_qtiles * a.B * a.H;
+  hipLaunchKernelGGL((fwd_pp_kernel<D, QT, CAUSAL>), dim3(total), dim3(512), 0, s,
+                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                     static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse, a.N, n_qtiles,
+                     total, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
 template <bool CAUSAL>
 hipError_t run_f32(const FwdArgs& a, hipStream_t s) {
   constexpr int BR = kWaves * 32;
@@ -564,7 +877,7 @@ hipError_t run_f32(const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
-  if (a.d == 64) return a.causal ? run_bf16<64, 2, 4, true>(a, s) : run_bf16<64, 2, 4, false>(a, s);
+  if (a.d == 64) return a.causal ? run_pp<64, 2, true>(a, s) : run_pp<64, 2, false>(a, s);
   return a.causal ? run_bf16<128, 1, 2, true>(a, s) : run_bf16<128, 1, 2, false>(a, s);
 }
 
