@@ -100,8 +100,9 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const __bf16* 
     for (int r = 0; r < kRound; ++r) {
       const int key = k0 + r * NS + slot;
       const bool ok = key < hi;
-      kr[r] = ok ? *reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + 8 * u) : u32x4{};
-      vr[r] = ok ? *reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + 8 * u) : u32x4{};
+      // the cache is streamed once: non-temporal loads keep it out of the caches
+      kr[r] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + 8 * u)) : u32x4{};
+      vr[r] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + 8 * u)) : u32x4{};
     }
     float s[kRound];
     float rmax = kNegInf;
@@ -173,13 +174,18 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const __bf16* 
   }
 }
 
+// Reduce step: one workgroup per (b, h).  Each lane owns 4 consecutive dims
+// and a subset of the chunks; it forms the weights e^(m_c - m) of its chunks
+// and reads their U_c rows with 16-byte loads, several chunks in flight, and
+// the per-dim partial sums are combined through LDS.
 template <int D>
 __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const float* __restrict__ ws, __bf16* __restrict__ O,
                                                                 float* __restrict__ LSE, int S, int BH) {
-  constexpr int G = kThreads / D;  // chunk groups working on the same d
-  __shared__ float sm_w[kThreads];
+  constexpr int LPR = D / 4;           // lanes per U row (4 dims each)
+  constexpr int RPW = kThreads / LPR;  // chunk rows read together by the workgroup
+  constexpr int UNR = 4;               // rows in flight per lane
   __shared__ float sm_red[kThreads];
-  __shared__ float sm_acc[G][D];
+  __shared__ f32x4 sm_acc[RPW][LPR];
 
   const int bh = blockIdx.x;
   const int tid = threadIdx.x;
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const float* __r
   const float* wm = ws + (int64_t)BH * S * D + (int64_t)bh * S;
   const float* wl = ws + (int64_t)BH * S * D + (int64_t)BH * S + (int64_t)bh * S;
 
-  // M = max_c m_c
+  // M = max_c m_c (natural-log units)
   float mx = kNegInf;
   for (int c = tid; c < S; c += kThreads) mx = fmaxf(mx, wm[c]);
   sm_red[tid] = mx;
@@ -200,23 +206,13 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const float* __r
   const float Ms = (M == kNegInf) ? 0.f : M;
   __syncthreads();
 
-  const int grp = tid / D, d = tid % D;
-  float acc = 0.f, lpart = 0.f;
-  for (int c0 = 0; c0 < S; c0 += kThreads) {
-    const int c = c0 + tid;
-    float w = 0.f;
-    if (c < S) {
-      const float mc = wm[c];
-      w = (mc == kNegInf) ? 0.f : fast_exp2((mc - Ms) * kLog2e);
-      lpart += w * wl[c];
-    }
-    sm_w[tid] = w;
-    __syncthreads();
-    const int n = min(kThreads, S - c0);
-    for (int cc = grp; cc < n; cc += G) acc += sm_w[cc] * wu[(int64_t)(c0 + cc) * D + d];
-    __syncthreads();
-  }
-  sm_acc[grp][d] = acc;
+  auto weight = [&](int c) {
+    const float mc = wm[c];
+    return (mc == kNegInf) ? 0.f : fast_exp2((mc - Ms) * kLog2e);
+  };
+  // l = sum_c w_c l_c
+  float lpart = 0.f;
+  for (int c = tid; c < S; c += kThreads) lpart += weight(c) * wl[c];
   sm_red[tid] = lpart;
   __syncthreads();
   for (int st = kThreads / 2; st > 0; st >>= 1) {
@@ -224,12 +220,31 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const float* __r
     __syncthreads();
   }
   const float lt = sm_red[0];
-  if (tid < D) {
-    float u = 0.f;
+
+  // U = sum_c w_c U_c
+  const int q = tid % LPR, r0 = tid / LPR;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int c0 = r0; c0 < S; c0 += RPW * UNR) {
+    f32x4 v[UNR];
+    float w[UNR];
 #pragma unroll
-    for (int gi = 0; gi < G; ++gi) u += sm_acc[gi][tid];
+    for (int k = 0; k < UNR; ++k) {
+      const int c = c0 + k * RPW;
+      v[k] = c < S ? *reinterpret_cast<const f32x4*>(wu + (int64_t)c * D + 4 * q) : f32x4{};
+      w[k] = c < S ? weight(c) : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < UNR; ++k) acc += w[k] * v[k];
+  }
+  sm_acc[r0][q] = acc;
+  __syncthreads();
+  if (tid < LPR) {
+    f32x4 u = sm_acc[0][tid];
+#pragma unroll
+    for (int r = 1; r < RPW; ++r) u += sm_acc[r][tid];
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    O[(int64_t)bh * D + tid] = (__bf16)(u * inv);
+    u32x2 o = {pack_bf16x2(u[0] * inv, u[1] * inv), pack_bf16x2(u[2] * inv, u[3] * inv)};
+    *reinterpret_cast<u32x2*>(O + (int64_t)bh * D + 4 * tid) = o;
     if (tid == 0 && LSE != nullptr) LSE[bh] = lt > 0.f ? M + fast_log2(lt) * kLn2 : kNegInf;
   }
 }
