@@ -121,6 +121,33 @@ def test_large_scores_no_overflow():
         assert_lse("LSE", lse, LSE)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_scores_rising_along_keys_move_the_reference(d, causal):
+    """Scores that grow by far more than 64 (log2 units) within every K/V tile.
+
+    The kernels keep the reference m of the exponentials at the first tile's
+    row max and move it to the exact running max only when a tile's partial
+    sums would exceed 2^64; here that happens on every tile for the even query
+    rows (q[0] = 8, k_j[0] = 2j, scale 1/8: score_j = 2j natural units, about
+    185 log2 units per 64-key tile), while the odd rows (q[0] = 0) never move
+    it, so both branches run inside the same wavefronts.
+    """
+    _say(f"rising scores d={d} causal={causal}")
+    N = 300
+    q, k, v = _inputs(21, 1, 2, N, d, torch.bfloat16, 0.125)
+    q = q.float()
+    k = k.float()
+    q[..., 0::2, 0] = 8.0
+    q[..., 1::2, 0] = 0.0
+    k[..., :, 0] = 2.0 * torch.arange(N, dtype=torch.float32)
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    o, lse = _run(q, k, v, 0.125, causal)
+    O, LSE = ref_fwd(widen(q), widen(k), widen(v), 0.125, causal)
+    assert_bar("O", o, O, torch.bfloat16)
+    assert_lse("LSE", lse, LSE)
+
+
 def test_deterministic_and_launch_on_side_stream():
     _say("determinism")
     q, k, v = (t.to(DEV) for t in _inputs(3, 2, 4, 333, 128, torch.bfloat16))
