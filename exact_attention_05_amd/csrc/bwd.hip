@@ -11,14 +11,16 @@
 //                    dS = P o (dP - D), dV^T += dO^T P, dK^T += Q^T dS.
 //   bwd_dq         : query tiles outer.  Each wavefront owns 32 queries,
 //                    keeps Q, dO in VGPRs and dQ^T as accumulator, and
-//                    streams 64-key tiles (K, K^T, V) through LDS:
+//                    streams 64-key tiles (K, V) through LDS:
 //                    S^T = K Q^T, dP^T = V dO^T, dS^T = P^T o (dP^T - D),
 //                    dQ^T += K^T dS^T.
 // dK and dQ are multiplied by the softmax scale at the end (section 8.8.4).
-// Products whose contraction runs over the sequence take their P / dS
-// operand straight from the accumulator of the previous product, and their
-// other operand from a transposed LDS copy whose 4-row chunks are permuted
-// to the accumulator's row order (the same scheme as V^T in the forward).
+// Tiles go HBM -> LDS with direct-to-LDS copies into the swizzled tile layout
+// of common.h, in a ring of buffers copied ahead of use.  Products that
+// contract over the sequence take their P / dS operand straight from the
+// accumulator of the previous product, and their other operand from the same
+// tile through transposing LDS reads whose 4-row chunks follow the
+// accumulator's row order (the scheme of V^T in the forward).
 #include "common.h"
 #include "launch.h"
 
@@ -27,81 +29,7 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
-constexpr int kPad = 8;
 constexpr int kT = 64;  // rows per streamed tile
-
-__device__ __forceinline__ int vt_chunk(int kc) { return (kc & ~3) | ((kc & 1) << 1) | ((kc >> 1) & 1); }
-
-// A 64 x D bf16 tile held by the workgroup as 4x4 blocks (4 rows x 8 bytes).
-template <int D>
-struct Blocks4 {
-  static constexpr int NB = kT * D / 16 / kThreads;
-  u32x2 r[NB][4];
-
-  __device__ __forceinline__ void load(const __bf16* src, int rows_valid, int tid) {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int id = tid + b * kThreads;
-      const int kc = id / (D / 4), dc = id % (D / 4);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int row = 4 * kc + rr;
-        r[b][rr] = row < rows_valid ? *reinterpret_cast<const u32x2*>(src + (int64_t)row * D + 4 * dc) : u32x2{};
-      }
-    }
-  }
-  __device__ __forceinline__ void store_rows(__bf16* dst, int stride, int tid) const {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int id = tid + b * kThreads;
-      const int kc = id / (D / 4), dc = id % (D / 4);
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) *reinterpret_cast<u32x2*>(dst + (4 * kc + rr) * stride + 4 * dc) = r[b][rr];
-    }
-  }
-  // dst is [D][stride]; row chunk kc lands at column 4 * vt_chunk(kc).
-  __device__ __forceinline__ void store_transposed(__bf16* dst, int stride, int tid) const {
-#pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const int id = tid + b * kThreads;
-      const int kc = id / (D / 4), dc = id % (D / 4);
-      const int pcol = 4 * vt_chunk(kc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int w = i >> 1;
-        const bool hi = i & 1;
-        uint32_t e[4];
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) e[rr] = hi ? (r[b][rr][w] >> 16) : (r[b][rr][w] & 0xffffu);
-        u32x2 out = {e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
-        *reinterpret_cast<u32x2*>(dst + (4 * dc + i) * stride + pcol) = out;
-      }
-    }
-  }
-};
-
-// A 64 x D bf16 tile held as 16-byte row chunks.
-template <int D>
-struct Chunks16 {
-  static constexpr int NC = kT * D / 8 / kThreads;
-  u32x4 r[NC];
-  __device__ __forceinline__ void load(const __bf16* src, int rows_valid, int tid) {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int id = tid + c * kThreads;
-      const int row = id / (D / 8), col = (id % (D / 8)) * 8;
-      r[c] = row < rows_valid ? *reinterpret_cast<const u32x4*>(src + (int64_t)row * D + col) : u32x4{};
-    }
-  }
-  __device__ __forceinline__ void store_rows(__bf16* dst, int stride, int tid) const {
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int id = tid + c * kThreads;
-      const int row = id / (D / 8), col = (id % (D / 8)) * 8;
-      *reinterpret_cast<u32x4*>(dst + row * stride + col) = r[c];
-    }
-  }
-};
 
 // Store a D^T x 32 accumulator tile set (lane: column l32, rows acc_row) as
 // rows of a [rows][D] bf16 tensor, multiplied by `mul`.
@@ -145,162 +73,231 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(const __bf16* 
 }
 
 // ---------------------------------------------------------------------------
-// dK, dV: key tiles outer
+// Per-lane LDS offsets shared by both kernels (tile layout of common.h):
+//   row operand of ks-slice ks, rows 32h + l32: roff[ks] + h * kHalf;
+//   transposing operand of 16-row slice t, dims 32mt..+31: toff[0/1][mt] + t * kTStep.
 // ---------------------------------------------------------------------------
 template <int D>
-struct DkdvLds {
-  static constexpr int kRow = D + kPad;   // Q, dO row-major [64][D]
-  static constexpr int kTRow = kT + kPad; // Q^T, dO^T [D][64]
-  static constexpr int kRowElems = kT * kRow;
-  static constexpr int kTElems = D * kTRow;
-  static constexpr int kBufBf16 = 2 * kRowElems + 2 * kTElems;
-  static constexpr int kBufBytes = kBufBf16 * 2 + 2 * kT * 4;  // + LSE2, D
+struct TileOffsets {
+  using T = TileLayout<D>;
+  static constexpr int kHalf = 32 * D * 2;   // 32 rows further: same swizzle phase
+  static constexpr int kTStep = 16 * D * 2;  // 16 rows further
+  int roff[D / 16];
+  int toff[2][D / 32];
+  __device__ __forceinline__ TileOffsets(int lane) {
+    const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) roff[ks] = T::offset(l32, 2 * ks + g);
+    const int sl = lane & 15, G = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) {
+        const int row = 8 * h + 4 * (G >> 1) + (sl >> 2);
+        const int dim = 32 * mt + 16 * (G & 1) + 4 * (sl & 3);
+        toff[h][mt] = T::offset(row, dim >> 3) + 8 * ((dim >> 2) & 1);
+      }
+  }
+  // transposed operand: 16 consecutive rows (slice t, in the accumulator's
+  // row order) x 32 dims, as an MFMA A operand
+  __device__ __forceinline__ bf16x8 tr(const unsigned char* tile, int t, int mt) const {
+    const u32x2 lo = lds_read_tr16(tile + toff[0][mt] + t * kTStep);
+    const u32x2 hi = lds_read_tr16(tile + toff[1][mt] + t * kTStep);
+    const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+    return bitcast<bf16x8>(w);
+  }
+  __device__ __forceinline__ bf16x8 row(const unsigned char* tile, int ks, int h) const {
+    return *reinterpret_cast<const bf16x8*>(tile + roff[ks] + h * kHalf);
+  }
 };
 
+// Copy geometry of one 64-row tile of a [rows][D] tensor: the wavefronts of
+// the workgroup split its D/8 copies of 1 KB (4 lines); lane l fills physical
+// chunk l % 16 of its line, i.e. the logical (row, chunk) the swizzle puts there.
+template <int D, int NW>
+struct TileCopy {
+  using T = TileLayout<D>;
+  static constexpr int kPerWave = (D / 8 + NW - 1) / NW;
+  int row[kPerWave], col[kPerWave], dst[kPerWave];
+  bool on[kPerWave];
+  __device__ __forceinline__ TileCopy(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int c = wave + NW * i;
+      on[i] = c < D / 8;
+      const int line = 4 * c + (lane >> 4);
+      int k, ch;
+      T::at(on[i] ? line : 0, lane & 15, k, ch);
+      row[i] = k;
+      col[i] = 8 * ch;
+      dst[i] = 4 * c * 256;
+    }
+  }
+  // rows past `nrows` read row nrows-1 (in bounds; masked by the caller)
+  __device__ __forceinline__ void issue(const __bf16* src, int r0, int nrows, unsigned char* tile) const {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i)
+      if (on[i]) {
+        const int r = min(r0 + row[i], nrows - 1);
+        global_to_lds16(src + (int64_t)r * D + col[i], tile + dst[i]);
+      }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// dK, dV: key tiles outer.  LDS buffer: Q tile | dO tile | LSE[64] | D[64].
+// ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int n_ktiles, int total_wg, float scale,
     float scale_log2) {
-  using Lds = DkdvLds<D>;
+  using T = TileLayout<D>;
   constexpr int BK = kWaves * 32;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * Lds::kBufBytes];
+  constexpr int NB = D == 64 ? 4 : 2;  // ring depth; tiles are copied NB/2 ahead
+  constexpr int kBuf = 2 * T::kBytes + 2 * kT * 4;
+  __shared__ __attribute__((aligned(1024))) unsigned char sb0[kBuf];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb1[kBuf];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb2[NB > 2 ? kBuf : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb3[NB > 2 ? kBuf : 16];
 
   const int lid = xcd_remap(blockIdx.x, total_wg);
   const int bh = lid / n_ktiles;
   const int ktile = lid % n_ktiles;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, held in an SGPR
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t base = (int64_t)bh * N * D;
   const int k0 = ktile * BK;
   const int kw0 = k0 + wave * 32;
   const int key = kw0 + l32;
 
+  const TileCopy<D, kWaves> cp(wave, lane);
+  const TileOffsets<D> of(lane);
+  const float* LSEh = LSE + (int64_t)bh * N;
+  const float* Dh = delta + (int64_t)bh * N;
+  // wavefront 0 copies the tile's LSE, wavefront 1 its D (64 words each)
+  auto issue_tile = [&](int it, unsigned char* buf) __attribute__((always_inline)) {
+    const int q0 = it * kT;
+    cp.issue(Q + base, q0, N, buf);
+    cp.issue(dO + base, q0, N, buf + T::kBytes);
+    if (wave < 2) {
+      const int r = min(q0 + lane, N - 1);
+      global_to_lds4((wave == 0 ? LSEh : Dh) + r, buf + 2 * T::kBytes + wave * kT * 4);
+    }
+  };
+  // direct-to-LDS copies issued per wavefront per tile
+  constexpr int kCopies = 2 * TileCopy<D, kWaves>::kPerWave;
+
+  const int i_begin = CAUSAL ? k0 / kT : 0;
+  const int i_end = (N + kT - 1) / kT;
+  const int ntiles = i_end - i_begin;
+  constexpr int A = NB / 2;
+#pragma unroll
+  for (int p = 0; p < A; ++p)
+    if (p < ntiles) issue_tile(i_begin + p, p == 0 ? sb0 : sb1);
+
   // K, V of this wavefront's 32 keys as B operands: lane holds row `key`, dims 16ks + 8g .. +7
   bf16x8 kB[D / 16], vB[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    if (key < N) {
-      kB[ks] = *reinterpret_cast<const bf16x8*>(K + base + (int64_t)key * D + 16 * ks + 8 * g);
-      vB[ks] = *reinterpret_cast<const bf16x8*>(V + base + (int64_t)key * D + 16 * ks + 8 * g);
-    } else {
-      kB[ks] = bf16x8{};
-      vB[ks] = bf16x8{};
-    }
+    kB[ks] = key < N ? *reinterpret_cast<const bf16x8*>(K + base + (int64_t)key * D + 16 * ks + 8 * g) : bf16x8{};
+    vB[ks] = key < N ? *reinterpret_cast<const bf16x8*>(V + base + (int64_t)key * D + 16 * ks + 8 * g) : bf16x8{};
   }
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) dk[mt] = dv[mt] = f32x16{};
 
-  const int i_begin = CAUSAL ? k0 / kT : 0;
-  const int i_end = (N + kT - 1) / kT;
-
-  Blocks4<D> qreg, doreg;
-  float lse_r = 0.f, del_r = 0.f;
-
-  auto gload = [&](int it) {
+  auto compute = [&](int it, const unsigned char* buf) __attribute__((always_inline)) {
     const int q0 = it * kT;
-    const int rows = min(kT, N - q0);
-    qreg.load(Q + base + (int64_t)q0 * D, rows, tid);
-    doreg.load(dO + base + (int64_t)q0 * D, rows, tid);
-    if (tid < kT) {
-      const int qi = q0 + tid;
-      lse_r = qi < N ? LSE[(int64_t)bh * N + qi] * kLog2e : __builtin_inff();
-      del_r = qi < N ? delta[(int64_t)bh * N + qi] : 0.f;
-    }
-  };
-  auto sstore = [&](int buf) {
-    __bf16* Qs = reinterpret_cast<__bf16*>(smem + buf * Lds::kBufBytes);
-    __bf16* dOs = Qs + Lds::kRowElems;
-    __bf16* Qt = dOs + Lds::kRowElems;
-    __bf16* dOt = Qt + Lds::kTElems;
-    float* ls = reinterpret_cast<float*>(dOt + Lds::kTElems);
-    qreg.store_rows(Qs, Lds::kRow, tid);
-    qreg.store_transposed(Qt, Lds::kTRow, tid);
-    doreg.store_rows(dOs, Lds::kRow, tid);
-    doreg.store_transposed(dOt, Lds::kTRow, tid);
-    if (tid < kT) {
-      ls[tid] = lse_r;
-      ls[kT + tid] = del_r;
-    }
-  };
-
-  if (i_begin < i_end) {
-    gload(i_begin);
-    sstore(0);
-  }
-  __syncthreads();
-
-  for (int it = i_begin; it < i_end; ++it) {
-    const int buf = (it - i_begin) & 1;
-    const int q0 = it * kT;
-    if (it + 1 < i_end) gload(it + 1);
-    const __bf16* Qs = reinterpret_cast<const __bf16*>(smem + buf * Lds::kBufBytes);
-    const __bf16* dOs = Qs + Lds::kRowElems;
-    const __bf16* Qt = dOs + Lds::kRowElems;
-    const __bf16* dOt = Qt + Lds::kTElems;
-    const float* ls = reinterpret_cast<const float*>(dOt + Lds::kTElems);
-
-    const bool active = !CAUSAL || q0 + kT - 1 >= kw0;
-    if (active) {
-      f32x16 sacc[2], dpacc[2];
-      sacc[0] = sacc[1] = dpacc[0] = dpacc[1] = f32x16{};
+    if (CAUSAL && q0 + kT - 1 < kw0) return;  // every query of the tile is above this wavefront's keys
+    const unsigned char* Qt = buf;
+    const unsigned char* Dt = buf + T::kBytes;
+    const float* ls = reinterpret_cast<const float*>(buf + 2 * T::kBytes);
+    const bool need_mask = (q0 + kT > N) || (CAUSAL && q0 < kw0 + 31);
+    // the two 32-query halves one after the other, so that only one pair of
+    // score accumulators is live
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      __builtin_amdgcn_sched_barrier(0);  // keep the halves apart in the schedule
+      f32x16 sacc = {}, dpacc = {};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
+        sacc = mfma32x32x16(of.row(Qt, ks, qh), kB[ks], sacc);
+        dpacc = mfma32x32x16(of.row(Dt, ks, qh), vB[ks], dpacc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // lane holds queries q0 + 32qh + acc_row(i, g) of key `key`; hidden
+      // pairs get S = -inf, hence P = 0 and dS = 0
+      if (need_mask) {
 #pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qs + (32 * qh + l32) * Lds::kRow + 16 * ks + 8 * g);
-          const bf16x8 ad = *reinterpret_cast<const bf16x8*>(dOs + (32 * qh + l32) * Lds::kRow + 16 * ks + 8 * g);
-          sacc[qh] = mfma32x32x16(aq, kB[ks], sacc[qh]);
-          dpacc[qh] = mfma32x32x16(ad, vB[ks], dpacc[qh]);
+        for (int i = 0; i < 16; ++i) {
+          const int qi = q0 + 32 * qh + acc_row(i, g);
+          if (qi >= N || (CAUSAL && key > qi)) sacc[i] = kNegInf;
         }
       }
-      const bool need_mask = CAUSAL && q0 < kw0 + 31;
-      // P = exp2(S*c - LSE2), dS = P o (dP - D); lane holds queries q0 + 32qh + acc_row(i, g)
+      // P = exp2(S*c - LSE*log2e), dS = P o (dP - D)
 #pragma unroll
-      for (int qh = 0; qh < 2; ++qh) {
+      for (int c = 0; c < 4; ++c) {
+        const int qo = 32 * qh + 8 * c + 4 * g;
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qo);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ls + kT + qo);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int qo = 32 * qh + 8 * c + 4 * g;
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qo);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(ls + kT + qo);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = 4 * c + r;
-            float p = fast_exp2(fmaf(sacc[qh][i], scale_log2, -l4[r]));
-            if (need_mask && key > q0 + qo + r) p = 0.f;
-            sacc[qh][i] = p;
-            dpacc[qh][i] = p * (dpacc[qh][i] - d4[r]);
-          }
+        for (int r = 0; r < 4; ++r) {
+          const int i = 4 * c + r;
+          const float p = fast_exp2(fmaf(sacc[i], scale_log2, -l4[r] * kLog2e));
+          sacc[i] = p;
+          dpacc[i] = p * (dpacc[i] - d4[r]);
         }
       }
-      bf16x8 pb[4], sb[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int tt = 0; tt < 2; ++tt) {
         float x[8], y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          x[e] = sacc[t >> 1][8 * (t & 1) + e];
-          y[e] = dpacc[t >> 1][8 * (t & 1) + e];
+          x[e] = sacc[8 * tt + e];
+          y[e] = dpacc[8 * tt + e];
         }
-        pb[t] = pack_bf16x8(x);
-        sb[t] = pack_bf16x8(y);
-      }
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
+        const bf16x8 pb = pack_bf16x8(x);
+        const bf16x8 sbf = pack_bf16x8(y);
 #pragma unroll
         for (int mt = 0; mt < D / 32; ++mt) {
-          const bf16x8 ado = *reinterpret_cast<const bf16x8*>(dOt + (32 * mt + l32) * Lds::kTRow + 16 * t + 8 * g);
-          const bf16x8 aq = *reinterpret_cast<const bf16x8*>(Qt + (32 * mt + l32) * Lds::kTRow + 16 * t + 8 * g);
-          dv[mt] = mfma32x32x16(ado, pb[t], dv[mt]);
-          dk[mt] = mfma32x32x16(aq, sb[t], dk[mt]);
+          dv[mt] = mfma32x32x16(of.tr(Dt, 2 * qh + tt, mt), pb, dv[mt]);
+          dk[mt] = mfma32x32x16(of.tr(Qt, 2 * qh + tt, mt), sbf, dk[mt]);
         }
       }
     }
-    if (it + 1 < i_end) sstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  // Tile s of the sweep (query tile i_begin + s) is in buffer s % NB; at its
+  // step the copies of tile s + A go to buffer (s + A) % NB, which held tile
+  // s - A (NB = 2A) and is free after the barrier.
+  auto step = [&](int s, const unsigned char* buf, unsigned char* next) __attribute__((always_inline)) {
+    if (s + A - 1 < ntiles) {
+      if (wave < 2) wait_vm_at_most<(A - 1) * (kCopies + 1)>(); else wait_vm_at_most<(A - 1) * kCopies>();
+    } else {
+      wait_vm_at_most<0>();
+    }
+    lds_barrier();
+    if (s + A < ntiles) issue_tile(i_begin + s + A, next);
+    if (s < ntiles) compute(i_begin + s, buf);
+  };
+  // one exit per loop (steps past the end only wait and synchronise), so the
+  // accumulators keep their registers across iterations
+  if constexpr (NB == 4) {
+    for (int s = 0; s < ntiles; s += 4) {
+      step(s, sb0, sb2);
+      step(s + 1, sb1, sb3);
+      step(s + 2, sb2, sb0);
+      step(s + 3, sb3, sb1);
+    }
+  } else {
+    for (int s = 0; s < ntiles; s += 2) {
+      step(s, sb0, sb1);
+      step(s + 1, sb1, sb0);
+    }
   }
 
   if (key < N) {
@@ -310,51 +307,58 @@ __global__ __launch_bounds__(kThreads) void bwd_dkdv_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// dQ: query tiles outer
+// dQ: query tiles outer.  LDS buffer: K tile | V tile.
 // ---------------------------------------------------------------------------
-template <int D>
-struct DqLds {
-  static constexpr int kRow = D + kPad;   // K, V row-major [64][D]
-  static constexpr int kTRow = kT + kPad; // K^T [D][64]
-  static constexpr int kRowElems = kT * kRow;
-  static constexpr int kTElems = D * kTRow;
-  static constexpr int kBufElems = 2 * kRowElems + kTElems;
-};
-
 template <int D, bool CAUSAL>
-__global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V,
                                                           const __bf16* __restrict__ dO,
                                                           const float* __restrict__ LSE,
                                                           const float* __restrict__ delta, __bf16* __restrict__ dQ,
                                                           int N, int n_qtiles, int total_wg, float scale,
                                                           float scale_log2) {
-  using Lds = DqLds<D>;
+  using T = TileLayout<D>;
   constexpr int BQ = kWaves * 32;
-  __shared__ __attribute__((aligned(16))) __bf16 smem[2 * Lds::kBufElems];
+  constexpr int NB = D == 64 ? 4 : 2;
+  constexpr int kBuf = 2 * T::kBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char sb0[kBuf];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb1[kBuf];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb2[NB > 2 ? kBuf : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb3[NB > 2 ? kBuf : 16];
 
   const int lid = xcd_remap(blockIdx.x, total_wg);
   const int bh = lid / n_qtiles;
   int qtile = lid % n_qtiles;
-  if (CAUSAL) qtile = n_qtiles - 1 - qtile;
+  if (CAUSAL) qtile = n_qtiles - 1 - qtile;  // longest rows first
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, held in an SGPR
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t base = (int64_t)bh * N * D;
   const int q0 = qtile * BQ;
   const int qw0 = q0 + wave * 32;
   const int qr = qw0 + l32;
 
+  const TileCopy<D, kWaves> cp(wave, lane);
+  const TileOffsets<D> of(lane);
+  auto issue_tile = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
+    cp.issue(K + base, j * kT, N, buf);
+    cp.issue(V + base, j * kT, N, buf + T::kBytes);
+  };
+  constexpr int kCopies = 2 * TileCopy<D, kWaves>::kPerWave;
+
+  const int kend = CAUSAL ? min(N, q0 + BQ) : N;
+  const int ntiles = (kend + kT - 1) / kT;
+  constexpr int A = NB / 2;
+#pragma unroll
+  for (int p = 0; p < A; ++p)
+    if (p < ntiles) issue_tile(p, p == 0 ? sb0 : sb1);
+
   bf16x8 qB[D / 16], doB[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
-    if (qr < N) {
-      qB[ks] = *reinterpret_cast<const bf16x8*>(Q + base + (int64_t)qr * D + 16 * ks + 8 * g);
-      doB[ks] = *reinterpret_cast<const bf16x8*>(dO + base + (int64_t)qr * D + 16 * ks + 8 * g);
-    } else {
-      qB[ks] = bf16x8{};
-      doB[ks] = bf16x8{};
-    }
+    qB[ks] = qr < N ? *reinterpret_cast<const bf16x8*>(Q + base + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
+    doB[ks] = qr < N ? *reinterpret_cast<const bf16x8*>(dO + base + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
   }
   const float lse2 = qr < N ? LSE[(int64_t)bh * N + qr] * kLog2e : __builtin_inff();
   const float dl = qr < N ? delta[(int64_t)bh * N + qr] : 0.f;
@@ -363,85 +367,65 @@ __global__ __launch_bounds__(kThreads) void bwd_dq_kernel(const __bf16* __restri
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) dq[mt] = f32x16{};
 
-  const int kend = CAUSAL ? min(N, q0 + BQ) : N;
-  const int nblk = (kend + kT - 1) / kT;
-
-  Blocks4<D> kreg;
-  Chunks16<D> vreg;
-  auto gload = [&](int j) {
+  auto compute = [&](int j, const unsigned char* buf) __attribute__((always_inline)) {
     const int kb = j * kT;
-    const int rows = min(kT, N - kb);
-    kreg.load(K + base + (int64_t)kb * D, rows, tid);
-    vreg.load(V + base + (int64_t)kb * D, rows, tid);
-  };
-  auto sstore = [&](int buf) {
-    __bf16* Ks = smem + buf * Lds::kBufElems;
-    __bf16* Vs = Ks + Lds::kRowElems;
-    __bf16* Kt = Vs + Lds::kRowElems;
-    kreg.store_rows(Ks, Lds::kRow, tid);
-    kreg.store_transposed(Kt, Lds::kTRow, tid);
-    vreg.store_rows(Vs, Lds::kRow, tid);
-  };
-
-  if (nblk > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
-
-  for (int j = 0; j < nblk; ++j) {
-    const int kb = j * kT;
-    const int buf = j & 1;
-    if (j + 1 < nblk) gload(j + 1);
-    const __bf16* Ks = smem + buf * Lds::kBufElems;
-    const __bf16* Vs = Ks + Lds::kRowElems;
-    const __bf16* Kt = Vs + Lds::kRowElems;
-    const bool active = !CAUSAL || kb <= qw0 + 31;
-    if (active) {
-      f32x16 sacc[2], dpacc[2];
-      sacc[0] = sacc[1] = dpacc[0] = dpacc[1] = f32x16{};
+    if (CAUSAL && kb > qw0 + 31) return;  // every key of the tile is after this wavefront's queries
+    const unsigned char* Kt = buf;
+    const unsigned char* Vt = buf + T::kBytes;
+    const bool need_mask = (kb + kT > N) || (CAUSAL && kb + kT - 1 > qw0);
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      __builtin_amdgcn_sched_barrier(0);  // keep the halves apart in the schedule
+      f32x16 sacc = {}, dpacc = {};
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const bf16x8 ak = *reinterpret_cast<const bf16x8*>(Ks + (32 * kh + l32) * Lds::kRow + 16 * ks + 8 * g);
-          const bf16x8 av = *reinterpret_cast<const bf16x8*>(Vs + (32 * kh + l32) * Lds::kRow + 16 * ks + 8 * g);
-          sacc[kh] = mfma32x32x16(ak, qB[ks], sacc[kh]);
-          dpacc[kh] = mfma32x32x16(av, doB[ks], dpacc[kh]);
-        }
+        sacc = mfma32x32x16(of.row(Kt, ks, kh), qB[ks], sacc);
+        dpacc = mfma32x32x16(of.row(Vt, ks, kh), doB[ks], dpacc);
       }
-      const bool need_mask = (kb + kT > N) || (CAUSAL && kb + kT - 1 > qw0);
-#pragma unroll
-      for (int kh = 0; kh < 2; ++kh) {
+      __builtin_amdgcn_sched_barrier(0);
+      // lane holds keys kb + 32kh + acc_row(i, g) of query qr
+      if (need_mask) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float p = fast_exp2(fmaf(sacc[kh][i], scale_log2, -lse2));
-          if (need_mask) {
-            const int kk = kb + 32 * kh + acc_row(i, g);
-            if (kk >= N || (CAUSAL && kk > qr)) p = 0.f;
-          }
-          dpacc[kh][i] = p * (dpacc[kh][i] - dl);
+          const int kk = kb + 32 * kh + acc_row(i, g);
+          if (kk >= N || (CAUSAL && kk > qr)) sacc[i] = kNegInf;
         }
       }
-      bf16x8 sb[4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int i = 0; i < 16; ++i) {
+        const float p = fast_exp2(fmaf(sacc[i], scale_log2, -lse2));
+        dpacc[i] = p * (dpacc[i] - dl);
+      }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
         float y[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = dpacc[t >> 1][8 * (t & 1) + e];
-        sb[t] = pack_bf16x8(y);
-      }
+        for (int e = 0; e < 8; ++e) y[e] = dpacc[8 * tt + e];
+        const bf16x8 sbf = pack_bf16x8(y);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-#pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(Kt + (32 * mt + l32) * Lds::kTRow + 16 * t + 8 * g);
-          dq[mt] = mfma32x32x16(a, sb[t], dq[mt]);
-        }
+        for (int mt = 0; mt < D / 32; ++mt) dq[mt] = mfma32x32x16(of.tr(Kt, 2 * kh + tt, mt), sbf, dq[mt]);
       }
     }
-    if (j + 1 < nblk) sstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  auto step = [&](int s, const unsigned char* buf, unsigned char* next) __attribute__((always_inline)) {
+    if (s + A - 1 < ntiles) wait_vm_at_most<(A - 1) * kCopies>(); else wait_vm_at_most<0>();
+    lds_barrier();
+    if (s + A < ntiles) issue_tile(s + A, next);
+    if (s < ntiles) compute(s, buf);
+  };
+  if constexpr (NB == 4) {
+    for (int s = 0; s < ntiles; s += 4) {
+      step(s, sb0, sb2);
+      step(s + 1, sb1, sb3);
+      step(s + 2, sb2, sb0);
+      step(s + 3, sb3, sb1);
+    }
+  } else {
+    for (int s = 0; s < ntiles; s += 2) {
+      step(s, sb0, sb1);
+      step(s + 1, sb1, sb0);
+    }
   }
 
   if (qr < N) store_transposed_acc<D>(dQ + base + (int64_t)qr * D, dq, g, scale);

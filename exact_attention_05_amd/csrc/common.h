@@ -1,5 +1,6 @@
 // Device helpers shared by the gfx950 attention kernels: vector types, MFMA
-// wrappers, bf16 conversion, exp2, the launch-order remap for the 8 XCDs.
+// wrappers, bf16 conversion, exp2, LDS copies and reads, the LDS tile layout,
+// the launch-order remap for the 8 XCDs.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -89,6 +90,12 @@ __device__ __forceinline__ void global_to_lds16(const void* gptr, void* lds_base
   __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_base, 16, 0, 0);
 }
 
+// Direct HBM -> LDS copy of 4 bytes per lane: lane l's word lands at
+// lds_base + 4 * l.
+__device__ __forceinline__ void global_to_lds4(const void* gptr, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, (lds_void*)lds_base, 4, 0, 0);
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16).  Within every group of 16 lanes,
 // each lane names 8 bytes (4 consecutive 16-bit values); lane i of the group
 // receives, as its element j, element (i % 4) of the 8 bytes named by lane
@@ -122,6 +129,41 @@ __device__ __forceinline__ void wait_vm_at_most() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
+
+// ---------------------------------------------------------------------------
+// Tile layout in LDS.  A tile of 64 rows (keys or queries) x D bf16 is stored
+// row-major (row k, dims d) as a sequence of 256-byte lines -- 64 banks of 4
+// bytes --
+// and the 16-byte chunks inside a line are XOR-swizzled by a function of the
+// line index.  The swizzle is chosen so that
+//   * the row-operand reads (16 consecutive rows, one chunk each) and
+//   * the transposing reads (4 consecutive rows x 2 chunks x 2 halves)
+// of every 16-lane group touch 16 distinct bank groups.
+// d = 64: row k lives in line k/2, chunks 8*(k%2) .. 8*(k%2)+7.
+// d = 128: row k is line k.
+template <int D>
+struct TileLayout {
+  static constexpr int kLines = D / 2;        // 256-byte lines per tile
+  static constexpr int kBytes = kLines * 256;  // = 64 * D * 2
+  __device__ static __forceinline__ int swz(int line) {
+    if constexpr (D == 64) return ((line & 1) << 1) | ((line >> 1) & 1) | (line & 4);
+    else return ((line & 3) << 1) | ((line >> 2) & 1) | (line & 8);
+  }
+  // byte offset of logical 16-byte chunk c of row k
+  __device__ static __forceinline__ int offset(int k, int c) {
+    const int lin = k * (D * 2) + 16 * c;  // unswizzled byte offset
+    const int line = lin >> 8;
+    const int chunk = (lin >> 4) & 15;
+    return line * 256 + 16 * (chunk ^ swz(line));
+  }
+  // inverse: the (row, chunk) stored at physical chunk p of line `line`
+  __device__ static __forceinline__ void at(int line, int p, int& k, int& c) {
+    const int chunk = p ^ swz(line);
+    const int lin = line * 256 + 16 * chunk;
+    k = lin / (D * 2);
+    c = (lin % (D * 2)) / 16;
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Launch-order remap for 8 XCDs.

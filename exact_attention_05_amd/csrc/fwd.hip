@@ -35,39 +35,6 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kBc = 64;  // keys per K/V tile
 
-// K/V tile layout in LDS.  A tile of 64 keys x D bf16 is stored row-major
-// (key k, dims d) as a sequence of 256-byte lines -- 64 banks of 4 bytes --
-// and the 16-byte chunks inside a line are XOR-swizzled by a function of the
-// line index.  The swizzle is chosen so that
-//   * the K operand reads (16 consecutive keys, one chunk each) and
-//   * the transposing V reads (4 consecutive keys x 2 chunks x 2 halves)
-// of every 16-lane group touch 16 distinct bank groups.
-// d = 64: key k lives in line k/2, chunks 8*(k%2) .. 8*(k%2)+7.
-// d = 128: key k is line k.
-template <int D>
-struct TileLayout {
-  static constexpr int kLines = D / 2;        // 256-byte lines per tile
-  static constexpr int kBytes = kLines * 256;  // = 64 * D * 2
-  __device__ static __forceinline__ int swz(int line) {
-    if constexpr (D == 64) return ((line & 1) << 1) | ((line >> 1) & 1) | (line & 4);
-    else return ((line & 3) << 1) | ((line >> 2) & 1) | (line & 8);
-  }
-  // byte offset of logical 16-byte chunk c of key k
-  __device__ static __forceinline__ int offset(int k, int c) {
-    const int lin = k * (D * 2) + 16 * c;  // unswizzled byte offset
-    const int line = lin >> 8;
-    const int chunk = (lin >> 4) & 15;
-    return line * 256 + 16 * (chunk ^ swz(line));
-  }
-  // inverse: the (key, chunk) stored at physical chunk p of line `line`
-  __device__ static __forceinline__ void at(int line, int p, int& k, int& c) {
-    const int chunk = p ^ swz(line);
-    const int lin = line * 256 + 16 * chunk;
-    k = lin / (D * 2);
-    c = (lin % (D * 2)) / 16;
-  }
-};
-
 // Reference point of the exponentials.  The online state (m, l, U) is exact
 // for ANY reference m as long as l, U and the LSE all use the same one
 // (O = U / l and LSE = m + ln l cancel it), and numerically m only has to keep
