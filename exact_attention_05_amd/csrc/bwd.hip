@@ -31,6 +31,19 @@ constexpr int kWaves = 4;
 constexpr int kThreads = kWaves * 64;
 constexpr int kT = 64;  // rows per streamed tile
 
+// Logical work id -> (head, tile).  Heads are taken in groups of `group`
+// (the host picks about one eighth of them, one group per XCD share of the
+// grid); inside a group the ids run tile-major, so with causal masking the
+// heaviest tiles of all the group's heads start first and the light ones
+// fill the tail.
+__device__ __forceinline__ void head_tile(int lid, int n_tiles, int BH, int group, int& bh, int& tile) {
+  const int gi = lid / (group * n_tiles);
+  const int gsz = min(group, BH - gi * group);
+  const int r = lid - gi * group * n_tiles;
+  tile = r / gsz;
+  bh = gi * group + r % gsz;
+}
+
 // Store a D^T x 32 accumulator tile set (lane: column l32, rows acc_row) as
 // rows of a [rows][D] bf16 tensor, multiplied by `mul`.
 template <int D>
@@ -151,7 +164,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
-    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int n_ktiles, int total_wg, float scale,
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int BH, int n_ktiles, int group, float scale,
     float scale_log2) {
   using T = TileLayout<D>;
   constexpr int BK = kWaves * 32;
@@ -162,9 +175,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
   __shared__ __attribute__((aligned(1024))) unsigned char sb2[NB > 2 ? kBuf : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char sb3[NB > 2 ? kBuf : 16];
 
-  const int lid = xcd_remap(blockIdx.x, total_wg);
-  const int bh = lid / n_ktiles;
-  const int ktile = lid % n_ktiles;
+  int bh, ktile;  // key tile 0 has the most query tiles under causal masking
+  head_tile(xcd_remap(blockIdx.x, BH * n_ktiles), n_ktiles, BH, group, bh, ktile);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, held in an SGPR
@@ -315,7 +327,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
                                                           const __bf16* __restrict__ dO,
                                                           const float* __restrict__ LSE,
                                                           const float* __restrict__ delta, __bf16* __restrict__ dQ,
-                                                          int N, int n_qtiles, int total_wg, float scale,
+                                                          int N, int BH, int n_qtiles, int group, float scale,
                                                           float scale_log2) {
   using T = TileLayout<D>;
   constexpr int BQ = kWaves * 32;
@@ -326,10 +338,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
   __shared__ __attribute__((aligned(1024))) unsigned char sb2[NB > 2 ? kBuf : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char sb3[NB > 2 ? kBuf : 16];
 
-  const int lid = xcd_remap(blockIdx.x, total_wg);
-  const int bh = lid / n_qtiles;
-  int qtile = lid % n_qtiles;
-  if (CAUSAL) qtile = n_qtiles - 1 - qtile;  // longest rows first
+  int bh, qtile;
+  head_tile(xcd_remap(blockIdx.x, BH * n_qtiles), n_qtiles, BH, group, bh, qtile);
+  if (CAUSAL) qtile = n_qtiles - 1 - qtile;  // the last query tile sees the most keys
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, held in an SGPR
@@ -443,11 +454,12 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   if (e != hipSuccess) return e;
 
   const float scale_log2 = a.scale * kLog2e;
+  const int group = BH >= kNumXcd ? BH / kNumXcd : 1;
   const int n_kt = (a.N + kWaves * 32 - 1) / (kWaves * 32);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_kt * BH), dim3(kThreads), 0, s,
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                      static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), a.lse, a.delta,
-                     static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.N, n_kt, n_kt * BH, a.scale,
+                     static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.N, BH, n_kt, group, a.scale,
                      scale_log2);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
@@ -456,7 +468,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qt * BH), dim3(kThreads), 0, s,
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                      static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), a.lse, a.delta,
-                     static_cast<__bf16*>(a.dq), a.N, n_qt, n_qt * BH, a.scale, scale_log2);
+                     static_cast<__bf16*>(a.dq), a.N, BH, n_qt, group, a.scale, scale_log2);
   return hipGetLastError();
 }
 
