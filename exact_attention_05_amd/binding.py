@@ -181,7 +181,8 @@ def attn_bwd_workspace_bytes(B, H, N):
 def attn_bwd(q, k, v, o, dO, lse, scale=None, causal=False, dq=None, dk=None, dv=None, workspace=None):
     """dQ, dK, dV of attention from the forward's saved O and LSE.
 
-    Returns (dq, dk, dv, workspace); the workspace holds D = rowsum(dO o O).
+    Returns (dq, dk, dv, workspace); the workspace starts with D = rowsum(dO o O)
+    (B*H*N fp32 values).
     """
     B, H, N, d = q.shape
     dev = q.device

@@ -61,12 +61,31 @@ __device__ __forceinline__ void store_transposed_acc(__bf16* dst_row, const f32x
 }
 
 // ---------------------------------------------------------------------------
-// D = rowsum(dO o O)
+// Per-row terms, written to the workspace:
+//   delta[r] = D_r = rowsum(dO o O)_r                      (fp32)
+//   nl2[r]   = -LSE_r * log2(e)                           (fp32)
+//   dsplit[r]= (h, m, l, 0) in bf16 with h + m + l = -D_r to about 2^-24
+//              relative: each part is the bf16 rounding of what the previous
+//              parts left, and every remainder is exact in fp32.
+// The split lets an MFMA add -D_r to a whole row of dP: one extra K-slice
+// with (h, m, l) on the row side and (1, 1, 1) on the column side.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x2 split3_bf16(float x) {
+  const __bf16 h = (__bf16)x;
+  const float r1 = x - (float)h;
+  const __bf16 m = (__bf16)r1;
+  const __bf16 l = (__bf16)(r1 - (float)m);
+  const bf16x2 hm = {h, m};
+  const bf16x2 l0 = {l, (__bf16)0.f};
+  return u32x2{bitcast<uint32_t>(hm), bitcast<uint32_t>(l0)};
+}
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(const __bf16* __restrict__ O,
                                                                   const __bf16* __restrict__ dO,
-                                                                  float* __restrict__ delta, int64_t rows) {
+                                                                  const float* __restrict__ LSE,
+                                                                  float* __restrict__ delta, float* __restrict__ nl2,
+                                                                  u32x2* __restrict__ dsplit, int64_t rows) {
   constexpr int LPR = D / 8;  // lanes per row
   const int64_t row = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
   const int u = threadIdx.x % LPR;
@@ -82,7 +101,11 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(const __bf16* 
   }
 #pragma unroll
   for (int m = 1; m < LPR; m <<= 1) acc += shfl_xor_f32(acc, m);
-  if (row < rows && u == 0) delta[row] = acc;
+  if (row < rows && u == 0) {
+    delta[row] = acc;
+    nl2[row] = -LSE[row] * kLog2e;
+    dsplit[row] = split3_bf16(-acc);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -158,18 +181,18 @@ struct TileCopy {
 };
 
 // ---------------------------------------------------------------------------
-// dK, dV: key tiles outer.  LDS buffer: Q tile | dO tile | LSE[64] | D[64].
+// dK, dV: key tiles outer.  LDS buffer: Q tile | dO tile | nl2[64] | dsplit[64].
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ delta,
+    const __bf16* __restrict__ dO, const float* __restrict__ nl2, const u32x2* __restrict__ dsplit,
     __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int BH, int n_ktiles, int group, float scale,
     float scale_log2) {
   using T = TileLayout<D>;
   constexpr int BK = kWaves * 32;
   constexpr int NB = D == 64 ? 4 : 2;  // ring depth; tiles are copied NB/2 ahead
-  constexpr int kBuf = 2 * T::kBytes + 2 * kT * 4;
+  constexpr int kBuf = 2 * T::kBytes + kT * 4 + kT * 8;
   __shared__ __attribute__((aligned(1024))) unsigned char sb0[kBuf];
   __shared__ __attribute__((aligned(1024))) unsigned char sb1[kBuf];
   __shared__ __attribute__((aligned(1024))) unsigned char sb2[NB > 2 ? kBuf : 16];
@@ -188,16 +211,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
 
   const TileCopy<D, kWaves> cp(wave, lane);
   const TileOffsets<D> of(lane);
-  const float* LSEh = LSE + (int64_t)bh * N;
-  const float* Dh = delta + (int64_t)bh * N;
-  // wavefront 0 copies the tile's LSE, wavefront 1 its D (64 words each)
+  const float* nl2h = nl2 + (int64_t)bh * N;
+  const uint32_t* dsh = reinterpret_cast<const uint32_t*>(dsplit + (int64_t)bh * N);
+  // wavefront 0 copies the tile's nl2 (64 words), wavefronts 1 and 2 its
+  // dsplit (2 words per row, 32 rows each)
   auto issue_tile = [&](int it, unsigned char* buf) __attribute__((always_inline)) {
     const int q0 = it * kT;
     cp.issue(Q + base, q0, N, buf);
     cp.issue(dO + base, q0, N, buf + T::kBytes);
-    if (wave < 2) {
-      const int r = min(q0 + lane, N - 1);
-      global_to_lds4((wave == 0 ? LSEh : Dh) + r, buf + 2 * T::kBytes + wave * kT * 4);
+    if (wave == 0) {
+      global_to_lds4(nl2h + min(q0 + lane, N - 1), buf + 2 * T::kBytes);
+    } else if (wave < 3) {
+      const int w = 64 * (wave - 1) + lane;
+      const int r = min(q0 + (w >> 1), N - 1);
+      global_to_lds4(dsh + 2 * r + (w & 1), buf + 2 * T::kBytes + kT * 4 + 256 * (wave - 1));
     }
   };
   // direct-to-LDS copies issued per wavefront per tile
@@ -218,6 +245,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
     kB[ks] = key < N ? *reinterpret_cast<const bf16x8*>(K + base + (int64_t)key * D + 16 * ks + 8 * g) : bf16x8{};
     vB[ks] = key < N ? *reinterpret_cast<const bf16x8*>(V + base + (int64_t)key * D + 16 * ks + 8 * g) : bf16x8{};
   }
+  // column side of the -D slice: (1, 1, 1) in the first K-group, zero in the second
+  const bf16x8 ones3 = bitcast<bf16x8>(g == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) dk[mt] = dv[mt] = f32x16{};
@@ -228,6 +257,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
     const unsigned char* Qt = buf;
     const unsigned char* Dt = buf + T::kBytes;
     const float* ls = reinterpret_cast<const float*>(buf + 2 * T::kBytes);
+    const u32x2* dsl = reinterpret_cast<const u32x2*>(buf + 2 * T::kBytes + kT * 4);
     const bool need_mask = (q0 + kT > N) || (CAUSAL && q0 < kw0 + 31);
     // the two 32-query halves one after the other, so that only one pair of
     // score accumulators is live
@@ -235,6 +265,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
     for (int qh = 0; qh < 2; ++qh) {
       __builtin_amdgcn_sched_barrier(0);  // keep the halves apart in the schedule
       f32x16 sacc = {}, dpacc = {};
+      // dP - D: the row side of the extra slice is query row 32qh + l32's split of -D
+      const u32x2 dw = dsl[32 * qh + l32];
+      dpacc = mfma32x32x16(bitcast<bf16x8>(u32x4{dw[0], dw[1], 0u, 0u}), ones3, dpacc);
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         sacc = mfma32x32x16(of.row(Qt, ks, qh), kB[ks], sacc);
@@ -253,15 +286,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
       // P = exp2(S*c - LSE*log2e), dS = P o (dP - D)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const int qo = 32 * qh + 8 * c + 4 * g;
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + qo);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(ls + kT + qo);
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(ls + 32 * qh + 8 * c + 4 * g);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int i = 4 * c + r;
-          const float p = fast_exp2(fmaf(sacc[i], scale_log2, -l4[r] * kLog2e));
+          const float p = fast_exp2(fmaf(sacc[i], scale_log2, l4[r]));
           sacc[i] = p;
-          dpacc[i] = p * (dpacc[i] - d4[r]);
+          dpacc[i] = p * dpacc[i];
         }
       }
 #pragma unroll
@@ -288,7 +319,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
   // s - A (NB = 2A) and is free after the barrier.
   auto step = [&](int s, const unsigned char* buf, unsigned char* next) __attribute__((always_inline)) {
     if (s + A - 1 < ntiles) {
-      if (wave < 2) wait_vm_at_most<(A - 1) * (kCopies + 1)>(); else wait_vm_at_most<(A - 1) * kCopies>();
+      if (wave < 3) wait_vm_at_most<(A - 1) * (kCopies + 1)>(); else wait_vm_at_most<(A - 1) * kCopies>();
     } else {
       wait_vm_at_most<0>();
     }
@@ -325,8 +356,8 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void bwd_dq_kernel(const __bf16* __restrict__ Q, const __bf16* __restrict__ K,
                                                           const __bf16* __restrict__ V,
                                                           const __bf16* __restrict__ dO,
-                                                          const float* __restrict__ LSE,
-                                                          const float* __restrict__ delta, __bf16* __restrict__ dQ,
+                                                          const float* __restrict__ nl2,
+                                                          const u32x2* __restrict__ dsplit, __bf16* __restrict__ dQ,
                                                           int N, int BH, int n_qtiles, int group, float scale,
                                                           float scale_log2) {
   using T = TileLayout<D>;
@@ -371,8 +402,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
     qB[ks] = qr < N ? *reinterpret_cast<const bf16x8*>(Q + base + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
     doB[ks] = qr < N ? *reinterpret_cast<const bf16x8*>(dO + base + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
   }
-  const float lse2 = qr < N ? LSE[(int64_t)bh * N + qr] * kLog2e : __builtin_inff();
-  const float dl = qr < N ? delta[(int64_t)bh * N + qr] : 0.f;
+  const float nlse2 = qr < N ? nl2[(int64_t)bh * N + qr] : kNegInf;
+  // -D slice: this lane's query split of -D in the first K-group (zero in the
+  // second) against a row side of ones
+  const u32x2 dw = qr < N ? dsplit[(int64_t)bh * N + qr] : u32x2{0u, 0u};
+  const bf16x8 ndB = bitcast<bf16x8>(g == 0 ? u32x4{dw[0], dw[1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
+  const bf16x8 ones3 = bitcast<bf16x8>(u32x4{0x3F803F80u, 0x3F80u, 0u, 0u});
 
   f32x16 dq[D / 32];
 #pragma unroll
@@ -387,7 +422,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       __builtin_amdgcn_sched_barrier(0);  // keep the halves apart in the schedule
-      f32x16 sacc = {}, dpacc = {};
+      f32x16 sacc = {};
+      f32x16 dpacc = mfma32x32x16(ones3, ndB, f32x16{});
 #pragma unroll
       for (int ks = 0; ks < D / 16; ++ks) {
         sacc = mfma32x32x16(of.row(Kt, ks, kh), qB[ks], sacc);
@@ -404,8 +440,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float p = fast_exp2(fmaf(sacc[i], scale_log2, -lse2));
-        dpacc[i] = p * (dpacc[i] - dl);
+        const float p = fast_exp2(fmaf(sacc[i], scale_log2, nlse2));
+        dpacc[i] = p * dpacc[i];
       }
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -446,10 +482,13 @@ template <int D, bool CAUSAL>
 hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   const int64_t rows = (int64_t)BH * a.N;
+  // workspace: delta [rows] f32 | nl2 [rows] f32 | dsplit [rows] x 8 bytes
+  float* nl2 = a.delta + rows;
+  u32x2* dsplit = reinterpret_cast<u32x2*>(a.delta + 2 * rows);
   constexpr int rows_per_wg = kThreads / (D / 8);
   hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)((rows + rows_per_wg - 1) / rows_per_wg)),
                      dim3(kThreads), 0, s, static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(a.dO),
-                     a.delta, rows);
+                     a.lse, a.delta, nl2, dsplit, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -458,7 +497,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   const int n_kt = (a.N + kWaves * 32 - 1) / (kWaves * 32);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_kt * BH), dim3(kThreads), 0, s,
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), a.lse, a.delta,
+                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), nl2, dsplit,
                      static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.N, BH, n_kt, group, a.scale,
                      scale_log2);
   e = hipGetLastError();
@@ -467,7 +506,7 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   const int n_qt = (a.N + kWaves * 32 - 1) / (kWaves * 32);
   hipLaunchKernelGGL((bwd_dq_kernel<D, CAUSAL>), dim3(n_qt * BH), dim3(kThreads), 0, s,
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), a.lse, a.delta,
+                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), nl2, dsplit,
                      static_cast<__bf16*>(a.dq), a.N, BH, n_qt, group, a.scale, scale_log2);
   return hipGetLastError();
 }

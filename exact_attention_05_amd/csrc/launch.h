@@ -44,7 +44,8 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // [B*H*N] workspace
+  float* delta;  // workspace, 16 bytes per row: D [B*H*N] f32, -LSE*log2(e) [B*H*N] f32,
+                 // -D split into three bf16 parts [B*H*N] x 8 bytes
   int B, H, N, d;
   float scale;
   int causal;

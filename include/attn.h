@@ -124,8 +124,10 @@ attn_status attn_fwd_splitk_decode(const void* q, const void* k_cache, const voi
                                    float scale, void* stream);
 
 /*
- * Workspace size in bytes that attn_bwd needs: the fp32 vector
- * D = rowsum(dO o O), B*H*N values.  Returns 0 for invalid sizes.
+ * Workspace size in bytes that attn_bwd needs: 16 bytes per query row
+ * (B*H*N rows) for the per-row terms of the backward -- D = rowsum(dO o O)
+ * in fp32, -LSE*log2(e) in fp32, and -D split into three bf16 parts whose
+ * sum is -D to about fp32 precision.  Returns 0 for invalid sizes.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int N);
 
@@ -144,7 +146,7 @@ size_t attn_bwd_workspace_bytes(int B, int H, int N);
  *   lse            : [B, H, N] fp32 from attn_fwd with the same arguments
  *   dq, dk, dv     : [B, H, N, d] in `dtype` (written)
  *   workspace      : >= attn_bwd_workspace_bytes(B, H, N) bytes, 16-byte
- *                    aligned; holds D on return.
+ *                    aligned; its first B*H*N fp32 values hold D on return.
  *
  * Supported: ATTN_BF16 with d in {64, 128}.
  * Errors as attn_fwd, plus ATTN_ERR_WORKSPACE.

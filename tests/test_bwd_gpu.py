@@ -30,11 +30,13 @@ def _inputs(seed, B, H, N, d, device="cpu"):
     return [make_tensor(seed, n, B, H, N, d, torch.bfloat16, device=device) for n in ("q", "k", "v", "do")]
 
 
-def _gpu_bwd(q, k, v, dO, scale, causal):
+def _gpu_bwd(q, k, v, dO, scale, causal, want_lse=False):
     q, k, v, dO = (t.to(DEV) for t in (q, k, v, dO))
     o, lse = attn_fwd(q, k, v, scale=scale, causal=causal)
     dq, dk, dv, ws = attn_bwd(q, k, v, o, dO, lse, scale=scale, causal=causal)
     torch.cuda.synchronize()
+    if want_lse:
+        return dq, dk, dv, ws, o, lse
     return dq, dk, dv, ws, o
 
 
@@ -45,15 +47,24 @@ def test_bwd_ragged(N, d, causal):
     _say(f"bwd N={N} d={d} causal={causal}")
     q, k, v, dO = _inputs(N + d, 1, 2, N, d)
     scale = 1.0 / math.sqrt(d)
-    dq, dk, dv, ws, o = _gpu_bwd(q, k, v, dO, scale, causal)
+    dq, dk, dv, ws, o, lse = _gpu_bwd(q, k, v, dO, scale, causal, want_lse=True)
     Q, K, V, DO = (widen(t) for t in (q, k, v, dO))
     dQ, dK, dV = ref_bwd(Q, K, V, DO, scale, causal)
     assert_bar("dV", widen(dv), dV, torch.bfloat16)
     assert_bar("dK", widen(dk), dK, torch.bfloat16)
     assert_bar("dQ", widen(dq), dQ, torch.bfloat16)
-    # D = rowsum(dO o O) from the saved O
+    # workspace: D = rowsum(dO o O) from the saved O, then -LSE*log2(e), then
+    # -D as three bf16 parts (and a zero) whose sum is -D to ~fp32 precision
     D = (DO * widen(o)).sum(-1)
-    np.testing.assert_allclose(widen(ws).reshape(D.shape), D, rtol=1e-4, atol=1e-4)
+    rows = D.size
+    w = ws.cpu()
+    np.testing.assert_allclose(widen(w[:rows]).reshape(D.shape), D, rtol=1e-4, atol=1e-4)
+    np.testing.assert_allclose(widen(w[rows:2 * rows]).reshape(D.shape), -widen(lse.cpu()) * math.log2(math.e),
+                               rtol=1e-6, atol=1e-6)
+    parts = widen(w[2 * rows:4 * rows].contiguous().view(torch.bfloat16).reshape(rows, 4))
+    Dk = widen(w[:rows])
+    np.testing.assert_allclose(parts[:, :3].sum(-1), -Dk, rtol=1e-6, atol=1e-30)
+    assert np.all(parts[:, 3] == 0)
 
 
 def test_bwd_invariants():
