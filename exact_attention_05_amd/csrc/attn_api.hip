@@ -89,7 +89,7 @@ attn_status attn_fwd_splitk_decode(const void* q, const void* k_cache, const voi
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N) {
   if (B < 1 || H < 1 || N < 1) return 0;
-  return (size_t)B * (size_t)H * (size_t)N * 16;
+  return (size_t)B * (size_t)H * (size_t)N * 24;
 }
 
 attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dO, const float* lse,

@@ -67,8 +67,11 @@ __device__ __forceinline__ void store_transposed_acc(__bf16* dst_row, const f32x
 //   dsplit[r]= (h, m, l, 0) in bf16 with h + m + l = -D_r to about 2^-24
 //              relative: each part is the bf16 rounding of what the previous
 //              parts left, and every remainder is exact in fp32.
-// The split lets an MFMA add -D_r to a whole row of dP: one extra K-slice
-// with (h, m, l) on the row side and (1, 1, 1) on the column side.
+//   lsplit[r]= the same split of nl2[r] / (scale log2 e).
+// A split lets an MFMA add its value to a whole row of a product: one extra
+// K-slice with (h, m, l) on the row side and (1, 1, 1) on the column side.
+// dP - D comes out that way, and so does S + nl2 / (scale log2 e), whose
+// product with scale log2 e is the exponent of P.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ u32x2 split3_bf16(float x) {
   const __bf16 h = (__bf16)x;
@@ -85,7 +88,8 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(const __bf16* 
                                                                   const __bf16* __restrict__ dO,
                                                                   const float* __restrict__ LSE,
                                                                   float* __restrict__ delta, float* __restrict__ nl2,
-                                                                  u32x2* __restrict__ dsplit, int64_t rows) {
+                                                                  u32x2* __restrict__ dsplit, u32x2* __restrict__ lsplit,
+                                                                  float scale_log2, int64_t rows) {
   constexpr int LPR = D / 8;  // lanes per row
   const int64_t row = (int64_t)blockIdx.x * (kThreads / LPR) + threadIdx.x / LPR;
   const int u = threadIdx.x % LPR;
@@ -102,9 +106,11 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(const __bf16* 
 #pragma unroll
   for (int m = 1; m < LPR; m <<= 1) acc += shfl_xor_f32(acc, m);
   if (row < rows && u == 0) {
+    const float l2 = -LSE[row] * kLog2e;
     delta[row] = acc;
-    nl2[row] = -LSE[row] * kLog2e;
+    nl2[row] = l2;
     dsplit[row] = split3_bf16(-acc);
+    lsplit[row] = split3_bf16(l2 / scale_log2);
   }
 }
 
@@ -478,22 +484,439 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
   if (qr < N) store_transposed_acc<D>(dQ + base + (int64_t)qr * D, dq, g, scale);
 }
 
+// ---------------------------------------------------------------------------
+// d = 64: ping-pong variants.  Eight wavefronts, two per SIMD; each owns 32
+// keys (dK/dV) or 32 queries (dQ) and walks the streamed tiles in 32-row
+// halves.  Per half h it runs a matrix phase M(h) -- the score products of
+// half h, then the contraction of half h-1 into its accumulators -- and a
+// vector phase V(h) -- mask, exponentials, dS, bf16 packing, plus the LDS
+// reads of the row operands M(h+1) needs.  Every wavefront runs the same
+// sequence M(0) V(0) M(1) V(1) ... with a workgroup barrier between phases;
+// wavefronts 4-7 (trail) pass one extra barrier before starting and
+// wavefronts 0-3 (lead) one after finishing, so each trail wavefront runs one
+// phase behind the lead wavefront on its SIMD and the SIMD has one wavefront
+// issuing MFMAs while the other issues VALU work.  M(h) issues its
+// transposing reads first; they land while the score MFMAs run.
+//
+// Ring of 4 tile buffers: the copy of tile s+2 is issued at M(2s).  Each
+// wavefront waits for its own copies of tile s+1 before the barrier that
+// opens its M(2s+1); the trail's such barrier is the one that opens the
+// lead's V(2s+1), the first reader of tile s+1.  The last reader of tile s is
+// the trail's M(2s+2), well before tile s+4 is issued.
+// ---------------------------------------------------------------------------
+constexpr int kPPWaves = 8;
+constexpr int kPPThreads = kPPWaves * 64;
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dkdv_pp_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const u32x2* __restrict__ lsplit, const u32x2* __restrict__ dsplit,
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int BH, int n_ktiles, int group, float scale,
+    float scale_log2) {
+  constexpr int D = 64;
+  using T = TileLayout<D>;
+  constexpr int NW = kPPWaves;
+  constexpr int BK = NW * 32;
+  constexpr int kBuf = 2 * T::kBytes + 2 * kT * 8;  // Q | dO | dsplit | lsplit
+  __shared__ __attribute__((aligned(1024))) unsigned char sb0[kBuf];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb1[kBuf];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb2[kBuf];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb3[kBuf];
+
+  int bh, ktile;
+  head_tile(xcd_remap(blockIdx.x, BH * n_ktiles), n_ktiles, BH, group, bh, ktile);
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool lead = wave < 4;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int64_t base = (int64_t)bh * N * D;
+  const int k0 = ktile * BK;
+  const int kw0 = k0 + wave * 32;
+  const int key = kw0 + l32;
+
+  const TileCopy<D, NW> cp(wave, lane);
+  const TileOffsets<D> of(lane);
+  // wavefronts 0-1 copy the tile's dsplit, 2-3 its lsplit (2 words per row, 32 rows each)
+  const uint32_t* sph = reinterpret_cast<const uint32_t*>((wave < 2 ? dsplit : lsplit) + (int64_t)bh * N);
+  auto issue_tile = [&](int it, unsigned char* buf) __attribute__((always_inline)) {
+    const int q0 = it * kT;
+    cp.issue(Q + base, q0, N, buf);
+    cp.issue(dO + base, q0, N, buf + T::kBytes);
+    if (wave < 4) {
+      const int w = 64 * (wave & 1) + lane;
+      const int r = min(q0 + (w >> 1), N - 1);
+      global_to_lds4(sph + 2 * r + (w & 1), buf + 2 * T::kBytes + 256 * wave);
+    }
+  };
+  constexpr int kCopies = 2 * TileCopy<D, NW>::kPerWave;
+  // wait for this wavefront's copies of all tiles but the newest one
+  // (one_after) or of all tiles
+  auto wait_copies = [&](bool one_after) __attribute__((always_inline)) {
+    if (one_after) {
+      if (wave < 4) wait_vm_at_most<kCopies + 1>(); else wait_vm_at_most<kCopies>();
+    } else {
+      wait_vm_at_most<0>();
+    }
+  };
+
+  const int i_begin = CAUSAL ? k0 / kT : 0;
+  const int ntiles = (N + kT - 1) / kT - i_begin;
+  issue_tile(i_begin, sb0);
+  if (ntiles > 1) issue_tile(i_begin + 1, sb1);
+
+  bf16x8 kB[D / 16], vB[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    kB[ks] = key < N ? *reinterpret_cast<const bf16x8*>(K + base + (int64_t)key * D + 16 * ks + 8 * g) : bf16x8{};
+    vB[ks] = key < N ? *reinterpret_cast<const bf16x8*>(V + base + (int64_t)key * D + 16 * ks + 8 * g) : bf16x8{};
+  }
+  const bf16x8 ones3 = bitcast<bf16x8>(g == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
+  f32x16 dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) dk[mt] = dv[mt] = f32x16{};
+  f32x16 sacc, dpacc;             // S and dP - D of the current half
+  bf16x8 pb[2], sbf[2];           // P and dS of the previous half, bf16
+  bf16x8 rq[D / 16], rd[D / 16];  // Q and dO rows of the next half
+  u32x2 dw, lw;                   // its splits of -D and of nl2 / (scale log2 e)
+
+  auto read_rows = [&](const int QH, const unsigned char* buf) __attribute__((always_inline)) {
+    dw = reinterpret_cast<const u32x2*>(buf + 2 * T::kBytes)[32 * QH + l32];
+    lw = reinterpret_cast<const u32x2*>(buf + 2 * T::kBytes + kT * 8)[32 * QH + l32];
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      rq[ks] = of.row(buf, ks, QH);
+      rd[ks] = of.row(buf + T::kBytes, ks, QH);
+    }
+  };
+
+  // M: S + nl2 / (scale log2 e) and dP - D of the current half (rows read
+  // by the previous phase), then dV^T += dO^T P, dK^T += Q^T dS of the
+  // previous half (tile at bprev, half 1 - QH).
+  auto mph = [&](const int QH, const unsigned char* bprev, const bool do_acc, const bool do_scores)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    const int QP = 1 - QH;
+    bf16x8 tq[2][D / 32], td[2][D / 32];
+    if (do_acc) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) {
+          td[tt][mt] = of.tr(bprev + T::kBytes, 2 * QP + tt, mt);
+          tq[tt][mt] = of.tr(bprev, 2 * QP + tt, mt);
+        }
+    }
+    if (do_scores) {
+      dpacc = mfma32x32x16(bitcast<bf16x8>(u32x4{dw[0], dw[1], 0u, 0u}), ones3, f32x16{});
+      sacc = mfma32x32x16(bitcast<bf16x8>(u32x4{lw[0], lw[1], 0u, 0u}), ones3, f32x16{});
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        sacc = mfma32x32x16(rq[ks], kB[ks], sacc);
+        dpacc = mfma32x32x16(rd[ks], vB[ks], dpacc);
+      }
+    }
+    if (do_acc) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) {
+          dv[mt] = mfma32x32x16(td[tt][mt], pb[tt], dv[mt]);
+          dk[mt] = mfma32x32x16(tq[tt][mt], sbf[tt], dk[mt]);
+        }
+    }
+    if (do_acc && do_scores) {
+      __builtin_amdgcn_sched_group_barrier(0x0100, 8 * (D / 32), 0);
+      __builtin_amdgcn_sched_group_barrier(0x0008, 2 + 2 * (D / 16) + 4 * (D / 32), 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // V: P = exp2((S + nl2 / c) c) with c = scale log2 e (0 where hidden),
+  // dS = P o (dP - D) for the queries qa .. qa+31, packed to bf16; the rows
+  // of the next half are read meanwhile (from bnext, half NQH).
+  auto vph = [&](int qa, const bool next, const int NQH, const unsigned char* bnext)
+      __attribute__((always_inline)) {
+    if (next) read_rows(NQH, bnext);
+    if ((qa + 31 >= N) || (CAUSAL && qa < kw0 + 31)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int qi = qa + acc_row(i, g);
+        if (qi >= N || (CAUSAL && key > qi)) sacc[i] = kNegInf;
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float x[8], y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * tt + e;
+        const float p = fast_exp2(sacc[i] * scale_log2);
+        x[e] = p;
+        y[e] = p * dpacc[i];
+      }
+      pb[tt] = pack_bf16x8(x);
+      sbf[tt] = pack_bf16x8(y);
+    }
+    // keep the packing in this phase (the barrier orders memory only)
+    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(sbf[0]), "+v"(sbf[1]));
+  };
+
+  // Tile 0.
+  wait_copies(ntiles > 1);
+  lds_barrier();
+  if (!lead) lds_barrier();
+  if (ntiles > 2) issue_tile(i_begin + 2, sb2);
+  read_rows(0, sb0);
+  mph(0, sb0, false, true);
+  lds_barrier();
+  vph(i_begin * kT, true, 1, sb0);
+  if (ntiles > 1) wait_copies(ntiles > 2);
+  lds_barrier();
+  mph(1, sb0, true, true);
+  lds_barrier();
+  vph(i_begin * kT + 32, ntiles > 1, 0, sb1);
+  lds_barrier();
+  // Tile s >= 1 at cur, s-1 at prev, s+1 at nxt1; tile s+2 goes to nxt2.
+  auto step = [&](int s, const unsigned char* cur, const unsigned char* prev, const unsigned char* nxt1,
+                  unsigned char* nxt2) __attribute__((always_inline)) {
+    const int q0 = (i_begin + s) * kT;
+    if (s + 2 < ntiles) issue_tile(i_begin + s + 2, nxt2);
+    mph(0, prev, true, true);
+    lds_barrier();
+    vph(q0, true, 1, cur);
+    if (s + 1 < ntiles) wait_copies(s + 2 < ntiles);
+    lds_barrier();
+    mph(1, cur, true, true);
+    lds_barrier();
+    vph(q0 + 32, s + 1 < ntiles, 0, nxt1);
+    lds_barrier();
+  };
+  for (int s = 1; s < ntiles; s += 4) {
+    step(s, sb1, sb0, sb2, sb3);
+    if (s + 1 < ntiles) step(s + 1, sb2, sb1, sb3, sb0);
+    if (s + 2 < ntiles) step(s + 2, sb3, sb2, sb0, sb1);
+    if (s + 3 < ntiles) step(s + 3, sb0, sb3, sb1, sb2);
+  }
+  // Contraction of the last half.
+  {
+    const int t = (ntiles - 1) & 3;
+    const unsigned char* last = t == 0 ? sb0 : t == 1 ? sb1 : t == 2 ? sb2 : sb3;
+    mph(0, last, true, false);
+  }
+  if (lead) lds_barrier();
+
+  if (key < N) {
+    store_transposed_acc<D>(dV + base + (int64_t)key * D, dv, g, 1.f);
+    store_transposed_acc<D>(dK + base + (int64_t)key * D, dk, g, scale);
+  }
+}
+
+template <bool CAUSAL>
+__global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_pp_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    const __bf16* __restrict__ dO, const float* __restrict__ nl2, const u32x2* __restrict__ dsplit,
+    __bf16* __restrict__ dQ, int N, int BH, int n_qtiles, int group, float scale, float scale_log2) {
+  constexpr int D = 64;
+  using T = TileLayout<D>;
+  constexpr int NW = kPPWaves;
+  constexpr int BQ = NW * 32;
+  constexpr int kBuf = 2 * T::kBytes;
+  __shared__ __attribute__((aligned(1024))) unsigned char sb0[kBuf];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb1[kBuf];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb2[kBuf];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb3[kBuf];
+
+  int bh, qtile;
+  head_tile(xcd_remap(blockIdx.x, BH * n_qtiles), n_qtiles, BH, group, bh, qtile);
+  if (CAUSAL) qtile = n_qtiles - 1 - qtile;  // the last query tile sees the most keys
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool lead = wave < 4;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int64_t base = (int64_t)bh * N * D;
+  const int q0 = qtile * BQ;
+  const int qw0 = q0 + wave * 32;
+  const int qr = qw0 + l32;
+
+  const TileCopy<D, NW> cp(wave, lane);
+  const TileOffsets<D> of(lane);
+  auto issue_tile = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
+    cp.issue(K + base, j * kT, N, buf);
+    cp.issue(V + base, j * kT, N, buf + T::kBytes);
+  };
+  constexpr int kCopies = 2 * TileCopy<D, NW>::kPerWave;
+  auto wait_copies = [&](bool one_after) __attribute__((always_inline)) {
+    if (one_after) wait_vm_at_most<kCopies>(); else wait_vm_at_most<0>();
+  };
+
+  const int kend = CAUSAL ? min(N, q0 + BQ) : N;
+  const int ntiles = (kend + kT - 1) / kT;
+  issue_tile(0, sb0);
+  if (ntiles > 1) issue_tile(1, sb1);
+
+  bf16x8 qB[D / 16], doB[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) {
+    qB[ks] = qr < N ? *reinterpret_cast<const bf16x8*>(Q + base + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
+    doB[ks] = qr < N ? *reinterpret_cast<const bf16x8*>(dO + base + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
+  }
+  const float nlse2 = qr < N ? nl2[(int64_t)bh * N + qr] : kNegInf;
+  const u32x2 dwq = qr < N ? dsplit[(int64_t)bh * N + qr] : u32x2{0u, 0u};
+  const bf16x8 ndB = bitcast<bf16x8>(g == 0 ? u32x4{dwq[0], dwq[1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
+  const bf16x8 ones3 = bitcast<bf16x8>(u32x4{0x3F803F80u, 0x3F80u, 0u, 0u});
+  f32x16 dq[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) dq[mt] = f32x16{};
+  f32x16 sacc, dpacc;             // S^T and dP^T - D of the current half
+  bf16x8 sbf[2];                  // dS^T of the previous half, bf16
+  bf16x8 rk[D / 16], rv[D / 16];  // K and V rows of the next half
+
+  auto read_rows = [&](const int KH, const unsigned char* buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      rk[ks] = of.row(buf, ks, KH);
+      rv[ks] = of.row(buf + T::kBytes, ks, KH);
+    }
+  };
+
+  // M: S^T = K Q^T and dP^T - D of the current half, then dQ^T += K^T dS^T
+  // of the previous half (tile at bprev, half 1 - KH).
+  auto mph = [&](const int KH, const unsigned char* bprev, const bool do_acc, const bool do_scores)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    const int KP = 1 - KH;
+    bf16x8 tk[2][D / 32];
+    if (do_acc) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) tk[tt][mt] = of.tr(bprev, 2 * KP + tt, mt);
+    }
+    if (do_scores) {
+      dpacc = mfma32x32x16(ones3, ndB, f32x16{});
+      sacc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) {
+        sacc = mfma32x32x16(rk[ks], qB[ks], sacc);
+        dpacc = mfma32x32x16(rv[ks], doB[ks], dpacc);
+      }
+    }
+    if (do_acc) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) dq[mt] = mfma32x32x16(tk[tt][mt], sbf[tt], dq[mt]);
+    }
+    if (do_acc && do_scores) {
+      __builtin_amdgcn_sched_group_barrier(0x0100, 4 * (D / 32), 0);
+      __builtin_amdgcn_sched_group_barrier(0x0008, 1 + 2 * (D / 16) + 2 * (D / 32), 0);
+    }
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  // V: dS^T = P^T o (dP^T - D) for the keys ka .. ka+31, packed to bf16; the
+  // rows of the next half are read meanwhile.
+  auto vph = [&](int ka, const bool next, const int NKH, const unsigned char* bnext)
+      __attribute__((always_inline)) {
+    if (next) read_rows(NKH, bnext);
+    if ((ka + 31 >= N) || (CAUSAL && ka + 31 > qw0)) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int kk = ka + acc_row(i, g);
+        if (kk >= N || (CAUSAL && kk > qr)) sacc[i] = kNegInf;
+      }
+    }
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int i = 8 * tt + e;
+        y[e] = fast_exp2(fmaf(sacc[i], scale_log2, nlse2)) * dpacc[i];
+      }
+      sbf[tt] = pack_bf16x8(y);
+    }
+    asm volatile("" : "+v"(sbf[0]), "+v"(sbf[1]));
+  };
+
+  wait_copies(ntiles > 1);
+  lds_barrier();
+  if (!lead) lds_barrier();
+  if (ntiles > 2) issue_tile(2, sb2);
+  read_rows(0, sb0);
+  mph(0, sb0, false, true);
+  lds_barrier();
+  vph(0, true, 1, sb0);
+  if (ntiles > 1) wait_copies(ntiles > 2);
+  lds_barrier();
+  mph(1, sb0, true, true);
+  lds_barrier();
+  vph(32, ntiles > 1, 0, sb1);
+  lds_barrier();
+  auto step = [&](int s, const unsigned char* cur, const unsigned char* prev, const unsigned char* nxt1,
+                  unsigned char* nxt2) __attribute__((always_inline)) {
+    if (s + 2 < ntiles) issue_tile(s + 2, nxt2);
+    mph(0, prev, true, true);
+    lds_barrier();
+    vph(s * kT, true, 1, cur);
+    if (s + 1 < ntiles) wait_copies(s + 2 < ntiles);
+    lds_barrier();
+    mph(1, cur, true, true);
+    lds_barrier();
+    vph(s * kT + 32, s + 1 < ntiles, 0, nxt1);
+    lds_barrier();
+  };
+  for (int s = 1; s < ntiles; s += 4) {
+    step(s, sb1, sb0, sb2, sb3);
+    if (s + 1 < ntiles) step(s + 1, sb2, sb1, sb3, sb0);
+    if (s + 2 < ntiles) step(s + 2, sb3, sb2, sb0, sb1);
+    if (s + 3 < ntiles) step(s + 3, sb0, sb3, sb1, sb2);
+  }
+  {
+    const int t = (ntiles - 1) & 3;
+    const unsigned char* last = t == 0 ? sb0 : t == 1 ? sb1 : t == 2 ? sb2 : sb3;
+    mph(0, last, true, false);
+  }
+  if (lead) lds_barrier();
+
+  if (qr < N) store_transposed_acc<D>(dQ + base + (int64_t)qr * D, dq, g, scale);
+}
+
 template <int D, bool CAUSAL>
 hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   const int64_t rows = (int64_t)BH * a.N;
-  // workspace: delta [rows] f32 | nl2 [rows] f32 | dsplit [rows] x 8 bytes
+  // workspace: delta [rows] f32 | nl2 [rows] f32 | dsplit [rows] x 8 bytes | lsplit [rows] x 8 bytes
+  const float scale_log2 = a.scale * kLog2e;
   float* nl2 = a.delta + rows;
   u32x2* dsplit = reinterpret_cast<u32x2*>(a.delta + 2 * rows);
+  u32x2* lsplit = dsplit + rows;
   constexpr int rows_per_wg = kThreads / (D / 8);
   hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)((rows + rows_per_wg - 1) / rows_per_wg)),
                      dim3(kThreads), 0, s, static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(a.dO),
-                     a.lse, a.delta, nl2, dsplit, rows);
+                     a.lse, a.delta, nl2, dsplit, lsplit, scale_log2, rows);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
 
-  const float scale_log2 = a.scale * kLog2e;
   const int group = BH >= kNumXcd ? BH / kNumXcd : 1;
+  if constexpr (D == 64) {
+    const int n_kt = (a.N + kPPWaves * 32 - 1) / (kPPWaves * 32);
+    hipLaunchKernelGGL((bwd_dkdv_pp_kernel<CAUSAL>), dim3(n_kt * BH), dim3(kPPThreads), 0, s,
+                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                       static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), lsplit, dsplit,
+                       static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.N, BH, n_kt, group, a.scale,
+                       scale_log2);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int n_qt = (a.N + kPPWaves * 32 - 1) / (kPPWaves * 32);
+    hipLaunchKernelGGL((bwd_dq_pp_kernel<CAUSAL>), dim3(n_qt * BH), dim3(kPPThreads), 0, s,
+                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                       static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), nl2, dsplit,
+                       static_cast<__bf16*>(a.dq), a.N, BH, n_qt, group, a.scale, scale_log2);
+    return hipGetLastError();
+  }
   const int n_kt = (a.N + kWaves * 32 - 1) / (kWaves * 32);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_kt * BH), dim3(kThreads), 0, s,
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),

@@ -135,10 +135,15 @@ __device__ __forceinline__ void wait_vm_at_most() {
 // row-major (row k, dims d) as a sequence of 256-byte lines -- 64 banks of 4
 // bytes --
 // and the 16-byte chunks inside a line are XOR-swizzled by a function of the
-// line index.  The swizzle is chosen so that
-//   * the row-operand reads (16 consecutive rows, one chunk each) and
-//   * the transposing reads (4 consecutive rows x 2 chunks x 2 halves)
-// of every 16-lane group touch 16 distinct bank groups.
+// line index.  ds_read_b128 is served 16 lanes (256 bytes) per pass and
+// ds_read_b64_tr_b16 32 lanes per pass; the swizzle makes every pass touch
+// each of the 64 banks once:
+//   * row-operand reads: 16 consecutive rows, one chunk each -- the swizzle
+//     is a permutation of the chunk index over every 8 (d = 64) or 16
+//     (d = 128) aligned lines;
+//   * transposing reads: 4 consecutive rows x 4 aligned chunks -- the lines
+//     holding those rows XOR the 4-chunk block into distinct quarters (the
+//     low line bits drive the high swizzle bits).
 // d = 64: row k lives in line k/2, chunks 8*(k%2) .. 8*(k%2)+7.
 // d = 128: row k is line k.
 template <int D>
@@ -146,8 +151,8 @@ struct TileLayout {
   static constexpr int kLines = D / 2;        // 256-byte lines per tile
   static constexpr int kBytes = kLines * 256;  // = 64 * D * 2
   __device__ static __forceinline__ int swz(int line) {
-    if constexpr (D == 64) return ((line & 1) << 1) | ((line >> 1) & 1) | (line & 4);
-    else return ((line & 3) << 1) | ((line >> 2) & 1) | (line & 8);
+    if constexpr (D == 64) return ((line & 1) << 2) | ((line >> 1) & 3);
+    else return ((line & 3) << 2) | ((line >> 2) & 3);
   }
   // byte offset of logical 16-byte chunk c of row k
   __device__ static __forceinline__ int offset(int k, int c) {

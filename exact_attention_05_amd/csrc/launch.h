@@ -44,8 +44,8 @@ struct BwdArgs {
   void* dq;
   void* dk;
   void* dv;
-  float* delta;  // workspace, 16 bytes per row: D [B*H*N] f32, -LSE*log2(e) [B*H*N] f32,
-                 // -D split into three bf16 parts [B*H*N] x 8 bytes
+  float* delta;  // workspace, 24 bytes per row: D [B*H*N] f32, -LSE*log2(e) [B*H*N] f32,
+                 // three-part bf16 splits of -D and of -LSE/scale [B*H*N] x 8 bytes each
   int B, H, N, d;
   float scale;
   int causal;

@@ -124,10 +124,11 @@ attn_status attn_fwd_splitk_decode(const void* q, const void* k_cache, const voi
                                    float scale, void* stream);
 
 /*
- * Workspace size in bytes that attn_bwd needs: 16 bytes per query row
+ * Workspace size in bytes that attn_bwd needs: 24 bytes per query row
  * (B*H*N rows) for the per-row terms of the backward -- D = rowsum(dO o O)
- * in fp32, -LSE*log2(e) in fp32, and -D split into three bf16 parts whose
- * sum is -D to about fp32 precision.  Returns 0 for invalid sizes.
+ * in fp32, -LSE*log2(e) in fp32, and -D and -LSE/scale each split into three
+ * bf16 parts whose sum is the value to about fp32 precision.  Returns 0 for
+ * invalid sizes.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int N);
 

@@ -61,7 +61,7 @@ def test_workspace_sizes():
     assert lib.attn_decode_workspace_bytes(16, 32, 128, 256) == 16 * 32 * 256 * 130 * 4
     assert lib.attn_decode_workspace_bytes(0, 1, 64, 1) == 0
     assert lib.attn_decode_workspace_bytes(1, 1, 64, 0) == 0
-    assert lib.attn_bwd_workspace_bytes(2, 16, 4096) == 2 * 16 * 4096 * 16
+    assert lib.attn_bwd_workspace_bytes(2, 16, 4096) == 2 * 16 * 4096 * 24
     assert lib.attn_bwd_workspace_bytes(1, 1, 0) == 0
 
 

@@ -54,7 +54,8 @@ def test_bwd_ragged(N, d, causal):
     assert_bar("dK", widen(dk), dK, torch.bfloat16)
     assert_bar("dQ", widen(dq), dQ, torch.bfloat16)
     # workspace: D = rowsum(dO o O) from the saved O, then -LSE*log2(e), then
-    # -D as three bf16 parts (and a zero) whose sum is -D to ~fp32 precision
+    # -D and -LSE*log2(e)/(scale*log2(e)) as three bf16 parts (and a zero)
+    # whose sums are the values to ~fp32 precision
     D = (DO * widen(o)).sum(-1)
     rows = D.size
     w = ws.cpu()
@@ -65,6 +66,10 @@ def test_bwd_ragged(N, d, causal):
     Dk = widen(w[:rows])
     np.testing.assert_allclose(parts[:, :3].sum(-1), -Dk, rtol=1e-6, atol=1e-30)
     assert np.all(parts[:, 3] == 0)
+    lparts = widen(w[4 * rows:6 * rows].contiguous().view(torch.bfloat16).reshape(rows, 4))
+    nl2 = widen(w[rows:2 * rows])
+    np.testing.assert_allclose(lparts[:, :3].sum(-1), nl2 / (scale * math.log2(math.e)), rtol=1e-6, atol=1e-30)
+    assert np.all(lparts[:, 3] == 0)
 
 
 def test_bwd_invariants():
