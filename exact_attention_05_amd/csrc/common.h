@@ -171,6 +171,78 @@ struct TileLayout {
 };
 
 // ---------------------------------------------------------------------------
+// Per-lane LDS offsets of the MFMA operands in a TileLayout tile:
+//   row operand of ks-slice ks, rows 32h + l32: roff[ks] + h * kHalf;
+//   transposing operand of 16-row slice t, dims 32mt..+31: toff[0/1][mt] + t * kTStep.
+// ---------------------------------------------------------------------------
+template <int D>
+struct TileOffsets {
+  using T = TileLayout<D>;
+  static constexpr int kHalf = 32 * D * 2;   // 32 rows further: same swizzle phase
+  static constexpr int kTStep = 16 * D * 2;  // 16 rows further
+  int roff[D / 16];
+  int toff[2][D / 32];
+  __device__ __forceinline__ TileOffsets(int lane) {
+    const int g = lane >> 5, l32 = lane & 31;
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) roff[ks] = T::offset(l32, 2 * ks + g);
+    const int sl = lane & 15, G = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) {
+        const int row = 8 * h + 4 * (G >> 1) + (sl >> 2);
+        const int dim = 32 * mt + 16 * (G & 1) + 4 * (sl & 3);
+        toff[h][mt] = T::offset(row, dim >> 3) + 8 * ((dim >> 2) & 1);
+      }
+  }
+  // transposed operand: 16 consecutive rows (slice t, in the accumulator's
+  // row order) x 32 dims, as an MFMA A operand
+  __device__ __forceinline__ bf16x8 tr(const unsigned char* tile, int t, int mt) const {
+    const u32x2 lo = lds_read_tr16(tile + toff[0][mt] + t * kTStep);
+    const u32x2 hi = lds_read_tr16(tile + toff[1][mt] + t * kTStep);
+    const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
+    return bitcast<bf16x8>(w);
+  }
+  __device__ __forceinline__ bf16x8 row(const unsigned char* tile, int ks, int h) const {
+    return *reinterpret_cast<const bf16x8*>(tile + roff[ks] + h * kHalf);
+  }
+};
+
+// Copy geometry of one 64-row tile of a [rows][D] tensor: the wavefronts of
+// the workgroup split its D/8 copies of 1 KB (4 lines); lane l fills physical
+// chunk l % 16 of its line, i.e. the logical (row, chunk) the swizzle puts there.
+template <int D, int NW>
+struct TileCopy {
+  using T = TileLayout<D>;
+  static constexpr int kPerWave = (D / 8 + NW - 1) / NW;
+  int row[kPerWave], col[kPerWave], dst[kPerWave];
+  bool on[kPerWave];
+  __device__ __forceinline__ TileCopy(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int c = wave + NW * i;
+      on[i] = c < D / 8;
+      const int line = 4 * c + (lane >> 4);
+      int k, ch;
+      T::at(on[i] ? line : 0, lane & 15, k, ch);
+      row[i] = k;
+      col[i] = 8 * ch;
+      dst[i] = 4 * c * 256;
+    }
+  }
+  // rows past `nrows` read row nrows-1 (in bounds; masked by the caller)
+  __device__ __forceinline__ void issue(const __bf16* src, int r0, int nrows, unsigned char* tile) const {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i)
+      if (on[i]) {
+        const int r = min(r0 + row[i], nrows - 1);
+        global_to_lds16(src + (int64_t)r * D + col[i], tile + dst[i]);
+      }
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Launch-order remap for 8 XCDs.
 // Consecutive workgroup ids are handed to the XCDs round-robin, and each XCD
 // has its own L2.  Mapping hardware id -> logical id so that every XCD gets a

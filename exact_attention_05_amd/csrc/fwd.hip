@@ -7,24 +7,28 @@
 // tiles and O = U / l at the end.
 //
 // Mapping to the hardware:
-//   * one workgroup = 4 wavefronts = a query tile of 4*32*QT rows; each
-//     wavefront owns whole query rows (split-Q, "FlashAttention 1 和
+//   * every wavefront owns 32 whole query rows (split-Q, "FlashAttention 1 和
 //     FlashAttention 2 的区别", sections 7-8), so no cross-wave merge exists;
+//     d = 128: 4 wavefronts per workgroup (fwd_bf16_kernel); d = 64: 16
+//     wavefronts, four per SIMD in two groups one phase apart, so matrix and
+//     vector work of different wavefronts overlap (fwd_pp4_kernel);
 //   * Q stays in VGPRs as MFMA B operands for the whole K/V sweep;
-//   * K/V tiles of 64 keys go HBM -> VGPR -> LDS, double-buffered: the loads
-//     of tile j+1 are in flight while tile j is computed;
+//   * K/V tiles of 64 keys go HBM -> LDS with direct-to-LDS copies into a
+//     ring of buffers in the swizzled tile layout of common.h, copied ahead
+//     of their use;
 //   * the scores are computed transposed, S^T = K Q^T, with
 //     v_mfma_f32_32x32x16_bf16, so each lane holds 32 scores of ONE query:
 //     row max and row sum are in-lane plus one exchange with lane l^32;
 //   * the exponentials are exp2 with log2(e) folded into the scale
 //     (Triton tutorial, section 8.7.3); P~ is rounded to bf16 for the second
 //     product (section 8.4.4) while l sums the fp32 values;
-//   * O^T += V^T P~^T reuses the score accumulator directly as the B operand:
-//     V is stored transposed in LDS with its 4-key chunks permuted to match
-//     the accumulator's row order, so each lane reads 16 contiguous bytes;
+//   * O^T += V^T P~^T takes P~ straight from the score accumulator as the B
+//     operand; V^T comes from the row-major V tile through transposing LDS
+//     reads (ds_read_b64_tr_b16) whose 4-key chunks follow the accumulator's
+//     row order;
 //   * the causal mask is -inf on the diagonal tiles only; tiles above the
-//     diagonal are never loaded, and wavefronts whose rows lie entirely above
-//     a tile skip its arithmetic (Triton tutorial, section 8.7.1).
+//     diagonal are never loaded, and the longest query tiles are dispatched
+//     first (Triton tutorial, section 8.7.1).
 #include "common.h"
 #include "launch.h"
 
@@ -352,307 +356,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 }
 
 // ---------------------------------------------------------------------------
-// Ping-pong variant.  Eight wavefronts, two per SIMD: wavefronts 0-3 lead and
-// 4-7 trail by one phase.  Per K/V tile j a wavefront runs a matrix phase
-// (S_j^T = K_j Q^T for the whole tile, then O^T += V_{j-1}^T P~_{j-1}^T) and
-// a vector phase (mask, exponentials P~_j, row sums, reference check).  A
-// workgroup barrier separates phases, so on every SIMD one wavefront issues
-// matrix instructions while the other does the exponentials of its own tile,
-// instead of both competing for the same unit.  The matrix-phase wavefront
-// runs at raised issue priority so that its next product starts as soon as
-// the matrix unit frees up.  Online state, reference rules and LDS layout
-// are those of fwd_bf16_kernel; tile t's K is read in phases 2t and 2t+1,
-// its V in phases 2t+2 and 2t+3, and tile t+2 is copied at phase 2t.
-// ---------------------------------------------------------------------------
-template <int D, int QT, bool CAUSAL>
-__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void fwd_pp_kernel(
-    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg,
-    float scale_log2) {
-  using T = TileLayout<D>;
-  constexpr int NW = 8;
-  constexpr int BR = NW * 32 * QT;
-  constexpr int NCP = 2 * (D / 8) / NW;  // 1 KB copies per wavefront per tile
-  static_assert(NCP >= 1 && NCP * NW == 2 * (D / 8), "tile copy split");
-  __shared__ __attribute__((aligned(1024))) unsigned char sb0[2 * T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char sb1[2 * T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char sb2[2 * T::kBytes];
-  __shared__ __attribute__((aligned(1024))) unsigned char sb3[2 * T::kBytes];
-
-  const int lid = xcd_remap(blockIdx.x, total_wg);
-  const int bh = lid / n_qtiles;
-  int qtile = lid % n_qtiles;
-  if (CAUSAL) qtile = n_qtiles - 1 - qtile;  // longest rows first
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const bool lead = wave < 4;
-  const int g = lane >> 5, l32 = lane & 31;
-  const int64_t base = (int64_t)bh * N * D;
-  const __bf16* Qh = Q + base;
-  const __bf16* Kh = K + base;
-  const __bf16* Vh = V + base;
-  __bf16* Oh = O + base;
-
-  const int q0 = qtile * BR;
-  const int qw0 = q0 + wave * 32 * QT;
-  const int kend = CAUSAL ? min(N, q0 + BR) : N;
-  const int ntiles = (kend + kBc - 1) / kBc;
-
-  int ld_key[NCP], ld_col[NCP], ld_dst[NCP];
-  bool ld_v[NCP];
-#pragma unroll
-  for (int i = 0; i < NCP; ++i) {
-    const int c = wave * NCP + i;
-    const int cl = c % (D / 8);
-    const int line = 4 * cl + (lane >> 4);
-    int k, ch;
-    T::at(line, lane & 15, k, ch);
-    ld_key[i] = k;
-    ld_col[i] = 8 * ch;
-    ld_v[i] = c >= D / 8;
-    ld_dst[i] = (ld_v[i] ? T::kBytes : 0) + 4 * cl * 256;
-  }
-  auto issue_tile_copy = [&](int kb, unsigned char* kt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < NCP; ++i) {
-      const int row = min(kb + ld_key[i], N - 1);  // rows past the end are masked out
-      const int64_t off = (int64_t)row * D + ld_col[i];
-      global_to_lds16((ld_v[i] ? Vh : Kh) + off, kt + ld_dst[i]);
-    }
-  };
-
-  issue_tile_copy(0, sb0);
-  if (ntiles > 1) issue_tile_copy(kBc, sb1);
-
-  bf16x8 qf[QT][D / 16];
-#pragma unroll
-  for (int nt = 0; nt < QT; ++nt) {
-    const int qr = qw0 + nt * 32 + l32;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
-      qf[nt][ks] = qr < N ? *reinterpret_cast<const bf16x8*>(Qh + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
-  }
-
-  f32x16 oacc[QT][D / 32];
-  float m2[QT], lsum[QT], rs[QT];
-#pragma unroll
-  for (int nt = 0; nt < QT; ++nt) {
-    m2[nt] = kNegInf;
-    lsum[nt] = 0.f;
-#pragma unroll
-    for (int mt = 0; mt < D / 32; ++mt) oacc[nt][mt] = f32x16{};
-  }
-
-  int koff[D / 16];
-#pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = T::offset(l32, 2 * ks + g);
-  constexpr int kKhStep = 32 * D * 2;
-  int voff[2][D / 32];
-  {
-    const int s = lane & 15, G = lane >> 4;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
-        const int key = 8 * h + 4 * (G >> 1) + (s >> 2);
-        const int dim = 32 * mt + 16 * (G & 1) + 4 * (s & 3);
-        voff[h][mt] = T::offset(key, dim >> 3) + 8 * ((dim >> 2) & 1);
-      }
-  }
-  constexpr int kTStep = 16 * D * 2;
-
-  f32x16 sacc[QT][2];  // S^T of the current tile, two halves of 32 keys
-  bf16x8 pb[QT][4];    // P~ of the previous tile, four 16-key operands
-
-  // S^T = K Q^T for the tile whose K is at kt (both halves).
-  auto scores = [&](const unsigned char* kt) __attribute__((always_inline)) {
-#pragma unroll
-    for (int nt = 0; nt < QT; ++nt) sacc[nt][0] = sacc[nt][1] = f32x16{};
-    bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + koff[0]);
-#pragma unroll
-    for (int r = 0; r < 2 * (D / 16); ++r) {
-      const int hh = r / (D / 16), ks = r % (D / 16);
-      bf16x8 an = a;
-      if (r + 1 < 2 * (D / 16)) {
-        const int hn = (r + 1) / (D / 16), kn = (r + 1) % (D / 16);
-        an = *reinterpret_cast<const bf16x8*>(kt + koff[kn] + hn * kKhStep);
-      }
-#pragma unroll
-      for (int nt = 0; nt < QT; ++nt) sacc[nt][hh] = mfma32x32x16(a, qf[nt][ks], sacc[nt][hh]);
-      a = an;
-    }
-  };
-  // V^T operand of 16-key slice t, dims 32mt..+31 (two transposing reads).
-  auto vop = [&](const unsigned char* vt, int t, int mt) __attribute__((always_inline)) {
-    const u32x2 lo = lds_read_tr16(vt + voff[0][mt] + t * kTStep);
-    const u32x2 hi = lds_read_tr16(vt + voff[1][mt] + t * kTStep);
-    const u32x4 w = {lo[0], lo[1], hi[0], hi[1]};
-    return bitcast<bf16x8>(w);
-  };
-  // Matrix phase of tile j: O^T += V_{j-1}^T P~_{j-1}^T (V at vt) first, so
-  // that P~ dies before S_j^T = K_j Q^T (K at kt) is written; either part may
-  // be absent (first and last phases).  Each operand is read one product
-  // ahead of its use, so LDS latency overlaps the matrix unit.
-  auto mphase = [&](const unsigned char* kt, const unsigned char* vt, bool do_pv, bool do_qk)
-      __attribute__((always_inline)) {
-    __builtin_amdgcn_s_setprio(1);
-    if (do_pv) {
-      bf16x8 a = vop(vt, 0, 0);
-#pragma unroll
-      for (int r = 0; r < 4 * (D / 32); ++r) {
-        const int t = r / (D / 32), mt = r % (D / 32);
-        bf16x8 an = a;
-        if (r + 1 < 4 * (D / 32)) an = vop(vt, (r + 1) / (D / 32), (r + 1) % (D / 32));
-#pragma unroll
-        for (int nt = 0; nt < QT; ++nt) oacc[nt][mt] = mfma32x32x16(a, pb[nt][t], oacc[nt][mt]);
-        a = an;
-      }
-    }
-    if (do_qk) scores(kt);
-    __builtin_amdgcn_s_setprio(0);
-  };
-
-  // P~ = 2^(s*c - m) of query tile nt, rounded to bf16; rs = lane's fp32 sum.
-  auto expo = [&](int nt) __attribute__((always_inline)) {
-    float r4[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = fast_exp2(fmaf(sacc[nt][t >> 1][8 * (t & 1) + e], scale_log2, -m2[nt]));
-      r4[t] = ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
-      pb[nt][t] = pack_bf16x8(x);
-    }
-    rs[nt] = (r4[0] + r4[1]) + (r4[2] + r4[3]);
-  };
-
-  auto mask_tile = [&](int j) __attribute__((always_inline)) {
-    const int kb = j * kBc;
-    if ((kb + kBc > N) || (CAUSAL && kb + kBc - 1 > qw0)) {
-#pragma unroll
-      for (int nt = 0; nt < QT; ++nt) {
-        const int qr = qw0 + nt * 32 + l32;
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = kb + 32 * hh + acc_row(i, g);
-            const bool vis = key < N && (!CAUSAL || key <= qr);
-            if (!vis) sacc[nt][hh][i] = kNegInf;
-          }
-      }
-    }
-  };
-  auto row_max2 = [&](int nt) __attribute__((always_inline)) {
-    float mx = kNegInf;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[nt][0][i], sacc[nt][1][i]));
-    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-    return mx * scale_log2;
-  };
-
-  // Vector phase of tile j (K still in LDS at kt).  The scores die as the
-  // exponentials are formed; the rare rescue recomputes them from K.
-  auto vphase = [&](int j, const unsigned char* kt) __attribute__((always_inline)) {
-    mask_tile(j);
-    if (j == 0) {
-      // the reference m: exact row max of tile 0 (key 0 is visible to every row)
-#pragma unroll
-      for (int nt = 0; nt < QT; ++nt) m2[nt] = row_max2(nt);
-    }
-#pragma unroll
-    for (int nt = 0; nt < QT; ++nt) expo(nt);
-    bool bad = false;
-#pragma unroll
-    for (int nt = 0; nt < QT; ++nt) bad |= !(rs[nt] <= kSumLimit);
-    if (__builtin_expect(__ballot(bad) != 0, 0)) {
-      __builtin_amdgcn_sched_barrier(0);
-      scores(kt);
-      mask_tile(j);
-#pragma unroll
-      for (int nt = 0; nt < QT; ++nt) {
-        const float mx2 = row_max2(nt);
-        const bool grow = mx2 > m2[nt];
-        const float alpha = grow ? fast_exp2(m2[nt] - mx2) : 1.f;
-        m2[nt] = grow ? mx2 : m2[nt];
-        lsum[nt] *= alpha;
-#pragma unroll
-        for (int mt = 0; mt < D / 32; ++mt) oacc[nt][mt] *= alpha;
-        expo(nt);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#pragma unroll
-    for (int nt = 0; nt < QT; ++nt) lsum[nt] += rs[nt];
-  };
-
-  auto phase_barrier = [&]() __attribute__((always_inline)) { lds_barrier(); };
-
-  // One tile step = two phases.  kt: tile j's buffer, vprev: tile j-1's
-  // buffer, next: where tile j+2 goes.
-  auto tile_step = [&](int j, unsigned char* kt, unsigned char* vprev, unsigned char* next)
-      __attribute__((always_inline)) {
-    if (j + 1 < ntiles) wait_vm_at_most<NCP>(); else wait_vm_at_most<0>();
-    phase_barrier();
-    if (j + 2 < ntiles) issue_tile_copy((j + 2) * kBc, next);
-    const unsigned char* vt = vprev + T::kBytes;
-    if (lead) mphase(kt, vt, true, true);
-    else vphase(j - 1, vprev);
-    phase_barrier();
-    if (lead) vphase(j, kt);
-    else mphase(kt, vt, true, true);
-  };
-
-  // Tile 0: scores only.
-  if (ntiles > 1) wait_vm_at_most<NCP>(); else wait_vm_at_most<0>();
-  phase_barrier();
-  if (ntiles > 2) issue_tile_copy(2 * kBc, sb2);
-  if (lead) mphase(sb0, nullptr, false, true);
-  phase_barrier();
-  if (lead) vphase(0, sb0);
-  else mphase(sb0, nullptr, false, true);
-  for (int j = 1; j < ntiles; j += 4) {
-    tile_step(j, sb1, sb0, sb3);
-    if (j + 1 < ntiles) tile_step(j + 1, sb2, sb1, sb0); else break;
-    if (j + 2 < ntiles) tile_step(j + 2, sb3, sb2, sb1); else break;
-    if (j + 3 < ntiles) tile_step(j + 3, sb0, sb3, sb2); else break;
-  }
-  // Final phases: products of the last tile (ring slot (ntiles - 1) % 4).
-  {
-    const int tl = ntiles - 1;
-    const unsigned char* kt = (tl & 3) == 0 ? sb0 : (tl & 3) == 1 ? sb1 : (tl & 3) == 2 ? sb2 : sb3;
-    const unsigned char* vt = kt + T::kBytes;
-    phase_barrier();
-    if (lead) mphase(nullptr, vt, true, false);
-    else vphase(tl, kt);
-    phase_barrier();
-    if (!lead) mphase(nullptr, vt, true, false);
-  }
-
-#pragma unroll
-  for (int nt = 0; nt < QT; ++nt) {
-    const int qr = qw0 + nt * 32 + l32;
-    const float lt = lsum[nt] + shfl_xor_f32(lsum[nt], 32);
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    if (qr < N) {
-#pragma unroll
-      for (int mt = 0; mt < D / 32; ++mt) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const int d0 = 32 * mt + 8 * c + 4 * g;
-          u32x2 w = {pack_bf16x2(oacc[nt][mt][4 * c] * inv, oacc[nt][mt][4 * c + 1] * inv),
-                     pack_bf16x2(oacc[nt][mt][4 * c + 2] * inv, oacc[nt][mt][4 * c + 3] * inv)};
-          *reinterpret_cast<u32x2*>(Oh + (int64_t)qr * D + d0) = w;
-        }
-      }
-      if (g == 0 && LSE != nullptr)
-        LSE[(int64_t)bh * N + qr] = lt > 0.f ? (m2[nt] + fast_log2(lt)) * kLn2 : kNegInf;
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // fp32 inputs, d = 64: same loop with v_mfma_f32_32x32x2_f32; P~ stays fp32
 // and V needs no transpose (one fp32 per lane per MFMA operand).
 // ---------------------------------------------------------------------------
@@ -804,6 +507,224 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// d = 64 forward, four wavefronts per SIMD.  Sixteen wavefronts of 32 query
+// rows (512 rows per workgroup); wavefronts 0-7 lead and 8-15 trail by one
+// phase, so on every SIMD two wavefronts are in a matrix phase while two are
+// in a vector phase.  A single wavefront can issue only a fraction of what a
+// SIMD executes -- about three quarters of the MFMA rate and half of the VALU
+// rate -- so two of each kind keep both units busy.  Per 64-key tile j:
+// M(j) = O^T += V_{j-1}^T P~_{j-1}^T, then S_j^T = K_j Q^T (operands read from
+// LDS in the phase); V(j) = mask, exponentials, bf16 P~, row sums.
+//
+// Ring of 5 tile buffers (K | V): tile j+3 is copied at M(j) into the slot of
+// tile j-2, whose last reader (the trail's M(j-1)) is one phase earlier.
+// Each wavefront waits for its own copies of tile j+1 before the barrier that
+// opens its V(j); for the trail that barrier opens the lead's M(j+1), the
+// first reader of tile j+1.  Online state and reference rule as in
+// fwd_bf16_kernel.
+// ---------------------------------------------------------------------------
+template <bool CAUSAL>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void fwd_pp4_kernel(
+    const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
+    __bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg, float scale_log2) {
+  constexpr int D = 64;
+  using T = TileLayout<D>;
+  constexpr int NW = 16;
+  constexpr int BR = NW * 32;
+  __shared__ __attribute__((aligned(1024))) unsigned char sb0[2 * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb1[2 * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb2[2 * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb3[2 * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb4[2 * T::kBytes];
+
+  const int lid = xcd_remap(blockIdx.x, total_wg);
+  const int bh = lid / n_qtiles;
+  int qtile = lid % n_qtiles;
+  if (CAUSAL) qtile = n_qtiles - 1 - qtile;  // longest rows first
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool lead = wave < NW / 2;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int64_t base = (int64_t)bh * N * D;
+  const int q0 = qtile * BR;
+  const int qw0 = q0 + wave * 32;
+  const int qr = qw0 + l32;
+  const int kend = CAUSAL ? min(N, q0 + BR) : N;
+  const int ntiles = (kend + kBc - 1) / kBc;
+
+  // wavefronts 0-7 copy the K tile, 8-15 the V tile: one 1 KB copy each
+  const TileCopy<D, 8> cp(wave & 7, lane);
+  const __bf16* csrc = (wave < 8 ? K : V) + base;
+  const int coff = wave < 8 ? 0 : T::kBytes;
+  auto issue_tile = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
+    cp.issue(csrc, j * kBc, N, buf + coff);
+  };
+
+  issue_tile(0, sb0);
+  if (ntiles > 1) issue_tile(1, sb1);
+  if (ntiles > 2) issue_tile(2, sb2);
+
+  bf16x8 qB[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks)
+    qB[ks] = qr < N ? *reinterpret_cast<const bf16x8*>(Q + base + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
+
+  const TileOffsets<D> of(lane);
+  f32x16 oacc[D / 32];
+#pragma unroll
+  for (int mt = 0; mt < D / 32; ++mt) oacc[mt] = f32x16{};
+  float m2 = kNegInf, lsum = 0.f, rs = 0.f;
+  f32x16 sacc[2];  // S^T of the current tile, two halves of 32 keys
+  bf16x8 pb[4];    // P~ of the current tile, four 16-key operands
+
+  // S^T = K Q^T for the tile whose K is at kt.
+  auto scores = [&](const unsigned char* kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      sacc[hh] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 16; ++ks) sacc[hh] = mfma32x32x16(of.row(kt, ks, hh), qB[ks], sacc[hh]);
+    }
+  };
+  // M: O^T += V^T P~^T of the previous tile (at bprev), then S^T of this one (at kt).
+  auto mph = [&](const unsigned char* kt, const unsigned char* bprev, const bool do_pv, const bool do_s)
+      __attribute__((always_inline)) {
+    __builtin_amdgcn_s_setprio(1);
+    if (do_pv) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int mt = 0; mt < D / 32; ++mt) oacc[mt] = mfma32x32x16(of.tr(bprev + T::kBytes, t, mt), pb[t], oacc[mt]);
+    }
+    if (do_s) scores(kt);
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  auto mask_tile = [&](int j) __attribute__((always_inline)) {
+    const int kb = j * kBc;
+    if ((kb + kBc > N) || (CAUSAL && kb + kBc - 1 > qw0)) {
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb + 32 * hh + acc_row(i, g);
+          const bool vis = key < N && (!CAUSAL || key <= qr);
+          if (!vis) sacc[hh][i] = kNegInf;
+        }
+    }
+  };
+  auto row_max2 = [&]() __attribute__((always_inline)) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[1][i]));
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    return mx * scale_log2;
+  };
+  // P~ = 2^(s c - m), rounded to bf16; rs = the lane's fp32 sum.
+  auto expo = [&]() __attribute__((always_inline)) {
+    float r4[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = fast_exp2(fmaf(sacc[t >> 1][8 * (t & 1) + e], scale_log2, -m2));
+      r4[t] = ((x[0] + x[1]) + (x[2] + x[3])) + ((x[4] + x[5]) + (x[6] + x[7]));
+      pb[t] = pack_bf16x8(x);
+    }
+    rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+  };
+  // V(j): tile j's K at kt is read again only by the rare rescue.
+  auto vph = [&](int j, const unsigned char* kt) __attribute__((always_inline)) {
+    mask_tile(j);
+    if (j == 0) m2 = row_max2();  // the reference: exact row max of tile 0 (key 0 is visible to every row)
+    expo();
+    if (__builtin_expect(__ballot(!(rs <= kSumLimit)) != 0, 0)) {
+      // rare: move the reference to the exact running max and redo the tile
+      __builtin_amdgcn_sched_barrier(0);
+      scores(kt);
+      mask_tile(j);
+      const float mx2 = row_max2();
+      const bool grow = mx2 > m2;
+      const float alpha = grow ? fast_exp2(m2 - mx2) : 1.f;
+      m2 = grow ? mx2 : m2;
+      lsum *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < D / 32; ++mt) oacc[mt] *= alpha;
+      expo();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lsum += rs;
+    // keep the packing in this phase (the barrier orders memory only)
+    asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
+  };
+
+  // Tile 0 must have landed before the first barrier (tiles 1 and 2 may not).
+  if (ntiles > 2) wait_vm_at_most<2>(); else if (ntiles > 1) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
+  lds_barrier();
+  if (!lead) lds_barrier();
+  if (ntiles > 3) issue_tile(3, sb3);
+  mph(sb0, sb0, false, true);
+  // tile 1 (tiles 2 and 3 may still be in flight)
+  if (ntiles > 3) wait_vm_at_most<2>(); else if (ntiles > 2) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
+  lds_barrier();
+  vph(0, sb0);
+  // Tile j at cur, j-1 at prev; tile j+3 goes to far.
+  auto step = [&](int j, const unsigned char* cur, const unsigned char* prev, unsigned char* far)
+      __attribute__((always_inline)) {
+    lds_barrier();
+    if (j + 3 < ntiles) issue_tile(j + 3, far);
+    mph(cur, prev, true, true);
+    // tile j+1 (tiles j+2 and j+3 may still be in flight)
+    if (j + 3 < ntiles) wait_vm_at_most<2>(); else if (j + 2 < ntiles) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
+    lds_barrier();
+    vph(j, cur);
+  };
+  for (int j = 1; j < ntiles; j += 5) {
+    step(j, sb1, sb0, sb4);
+    if (j + 1 < ntiles) step(j + 1, sb2, sb1, sb0);
+    if (j + 2 < ntiles) step(j + 2, sb3, sb2, sb1);
+    if (j + 3 < ntiles) step(j + 3, sb4, sb3, sb2);
+    if (j + 4 < ntiles) step(j + 4, sb0, sb4, sb3);
+  }
+  lds_barrier();
+  {
+    const int t = (ntiles - 1) % 5;
+    const unsigned char* last = t == 0 ? sb0 : t == 1 ? sb1 : t == 2 ? sb2 : t == 3 ? sb3 : sb4;
+    mph(last, last, true, false);
+  }
+  if (lead) lds_barrier();
+
+  const float lt = lsum + shfl_xor_f32(lsum, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qr < N) {
+    __bf16* Oh = O + base;
+#pragma unroll
+    for (int mt = 0; mt < D / 32; ++mt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int d0 = 32 * mt + 8 * c + 4 * g;
+        u32x2 w = {pack_bf16x2(oacc[mt][4 * c] * inv, oacc[mt][4 * c + 1] * inv),
+                   pack_bf16x2(oacc[mt][4 * c + 2] * inv, oacc[mt][4 * c + 3] * inv)};
+        *reinterpret_cast<u32x2*>(Oh + (int64_t)qr * D + d0) = w;
+      }
+    if (g == 0 && LSE != nullptr) LSE[(int64_t)bh * N + qr] = lt > 0.f ? (m2 + fast_log2(lt)) * kLn2 : kNegInf;
+  }
+}
+
+template <bool CAUSAL>
+hipError_t run_pp4(const FwdArgs& a, hipStream_t s) {
+  constexpr int BR = 16 * 32;
+  const int n_qtiles = (a.N + BR - 1) / BR;
+  const int total = n_qtiles * a.B * a.H;
+  hipLaunchKernelGGL((fwd_pp4_kernel<CAUSAL>), dim3(total), dim3(1024), 0, s, static_cast<const __bf16*>(a.q),
+                     static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
+                     static_cast<__bf16*>(a.o), a.lse, a.N, n_qtiles, total, a.scale * kLog2e);
+  return hipGetLastError();
+}
+
 template <int D, int QT, int NBUF, bool CAUSAL>
 hipError_t run_bf16(const FwdArgs& a, hipStream_t s) {
   constexpr int BR = kWaves * 32 * QT;
@@ -814,18 +735,6 @@ hipError_t run_bf16(const FwdArgs& a, hipStream_t s) {
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                      static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse, a.N, n_qtiles,
                      total, scale_log2);
-  return hipGetLastError();
-}
-
-template <int D, int QT, bool CAUSAL>
-hipError_t run_pp(const FwdArgs& a, hipStream_t s) {
-  constexpr int BR = 8 * 32 * QT;
-  const int n_qtiles = (a.N + BR - 1) / BR;
-  const int total = n_qtiles * a.B * a.H;
-  hipLaunchKernelGGL((fwd_pp_kernel<D, QT, CAUSAL>), dim3(total), dim3(512), 0, s,
-                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                     static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse, a.N, n_qtiles,
-                     total, a.scale * kLog2e);
   return hipGetLastError();
 }
 
@@ -844,7 +753,7 @@ hipError_t run_f32(const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
-  if (a.d == 64) return a.causal ? run_pp<64, 2, true>(a, s) : run_pp<64, 2, false>(a, s);
+  if (a.d == 64) return a.causal ? run_pp4<true>(a, s) : run_pp4<false>(a, s);
   return a.causal ? run_bf16<128, 1, 2, true>(a, s) : run_bf16<128, 1, 2, false>(a, s);
 }
 
