@@ -14,7 +14,8 @@ Sources (web pages, cited by title and section):
   jzssuanfa): section 2 (the 4-token worked example), section 3 scenario B
   (FlashDecoding split-K with a pairwise reduction).
 * [FA1-vs-FA2] "FlashAttention 1 和 FlashAttention 2 的区别"
-  (iceferryling.github.io): section 6 (merging partial (m, l, O) states).
+  (iceferryling.github.io): section 6 (merging partial (m, l, O) states),
+  section 13 (decode is KV-cache bound; paged block tables).
 * [operatorworld] "FlashAttention tiling" (operatorworld.com): the online
   softmax update equations and degeneration checks; backward by recomputation.
 * [Triton-ch8] "8. FlashAttention 实战" (triton-tutorial.pages.dev):
@@ -37,4 +38,6 @@ from .attention_ref import (  # noqa: F401
     merge_partials_tree,
     ref_splitk_decode,
     decode_chunk_bounds,
+    gather_paged_rows,
+    ref_paged_decode,
 )

@@ -49,7 +49,7 @@ def _softmax_rows(S):
     Returns (P, m, l): m is the row max, l = sum_j exp(S_ij - m_i) and
     P = exp(S - m) / l.  Rows that are all -inf give P = 0, m = -inf, l = 0.
     """
-    m = S.max(axis=1)
+    m = S.max(axis=1, initial=NEG_INF)
     has_key = np.isfinite(m)
     E = np.zeros_like(S)
     E[has_key] = np.exp(S[has_key] - m[has_key, None])
@@ -272,3 +272,43 @@ def ref_splitk_decode(q, k, v, scale, num_splits):
     for h in np.ndindex(*lead):
         O[h][0], LSE[h][0] = merge_partials_tree(U[h], m[h], l[h])
     return O, LSE
+
+
+def gather_paged_rows(pool, block_table, seq_len, h):
+    """Rows 0 .. seq_len-1 of head h of one sequence stored in a block pool.
+
+    The pages name the paged block table as the KV-cache layout of decode
+    kernels ([FA1-vs-FA2] section 13) without fixing it; the reading used
+    here: the cache is a pool of fixed-size blocks, pool[blk, h, r, :] is row
+    r of block blk for head h, and block_table[j] is the pool block holding
+    the sequence's logical block j, so token t is row t % bs of block
+    block_table[t // bs].  Returns [seq_len, d].
+    """
+    pool = _f64(pool)
+    bs = pool.shape[2]
+    rows = [pool[int(block_table[t // bs]), h, t % bs] for t in range(seq_len)]
+    return np.array(rows).reshape(seq_len, pool.shape[3])
+
+
+def ref_paged_decode(q, k_pool, v_pool, block_table, seq_lens, scale):
+    """Decode of one query row per (b, h) against a paged KV cache.
+
+    q: [B, H, 1, d]; k_pool, v_pool: [num_blocks, H, bs, d];
+    block_table: [B, max_blocks]; seq_lens: [B].  For every (b, h) the
+    sequence's keys and values are gathered through the block table and the
+    result is plain attention of the single query over all of them (the
+    query sees every key, as in the dense decode): (O [B, H, 1, d],
+    LSE [B, H, 1]); a sequence of length 0 gives O = 0 and LSE = -inf.
+    """
+    q = _f64(q)
+    B, H = q.shape[0], q.shape[1]
+    O = np.zeros(q.shape[:-1] + (v_pool.shape[-1],))
+    LSE = np.full(q.shape[:-1], NEG_INF)
+    for b in range(B):
+        n = int(seq_lens[b])
+        for h in range(H):
+            kb = gather_paged_rows(k_pool, block_table[b], n, h)
+            vb = gather_paged_rows(v_pool, block_table[b], n, h)
+            O[b, h], LSE[b, h] = ref_fwd(q[b, h], kb, vb, scale)
+    return O, LSE
+

@@ -356,6 +356,87 @@ def test_decode_uniform_and_ones():
 
 
 # ---------------------------------------------------------------------------
+# Paged KV-cache decode ([FA1-vs-FA2] section 13 names the paged block table)
+# ---------------------------------------------------------------------------
+
+def _scatter_to_pool(k, bs, num_blocks, seed):
+    """Cut a dense cache [B, H, L, d] into blocks of bs rows and place them at
+    random distinct pool slots; returns (pool, table) with the unused slots
+    filled with noise."""
+    B, H, L, d = k.shape
+    nb = -(-L // bs)
+    rng = np.random.default_rng(seed)
+    slots = rng.permutation(num_blocks)[:B * nb].reshape(B, nb)
+    pool = rng.standard_normal((num_blocks, H, bs, d)) * 100.0
+    for b in range(B):
+        for j in range(nb):
+            rows = k[b, :, j * bs:(j + 1) * bs]
+            pool[slots[b, j], :, :rows.shape[1]] = rows
+    return pool, slots
+
+
+@pytest.mark.parametrize("bs", [1, 4, 16])
+def test_paged_decode_equals_dense_on_truncated_cache(bs):
+    """Blocks scattered to random pool slots, ragged lengths: the result is the
+    dense decode over each sequence's first seq_len keys."""
+    B, H, L, d = 3, 2, 37, 5
+    q = _rand((B, H, 1, d), 50)
+    k, v = _rand((B, H, L, d), 51), _rand((B, H, L, d), 52)
+    nblk = B * (-(-L // bs)) + 3
+    kp, tab = _scatter_to_pool(k, bs, nblk, 53)
+    vp = np.zeros_like(kp)
+    for b in range(B):
+        for j in range(tab.shape[1]):
+            rows = v[b, :, j * bs:(j + 1) * bs]
+            vp[tab[b, j], :, :rows.shape[1]] = rows
+    lens = np.array([L, 1, 20])
+    O, LSE = ar.ref_paged_decode(q, kp, vp, tab, lens, 0.6)
+    for b in range(B):
+        n = lens[b]
+        O1, L1 = ar.ref_splitk_decode(q[b:b + 1], k[b:b + 1, :, :n], v[b:b + 1, :, :n], 0.6, 3)
+        np.testing.assert_allclose(O[b], O1[0], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(LSE[b], L1[0], rtol=1e-13)
+
+
+def test_paged_decode_brute_force_tiny():
+    """One sequence of 5 tokens in blocks of 2 at pool slots (3, 0, 2): the
+    weights written out term by term."""
+    d = 2
+    kp, vp = _rand((4, 1, 2, d), 54), _rand((4, 1, 2, d), 55)
+    q = _rand((1, 1, 1, d), 56)
+    table = np.array([[3, 0, 2]])
+    keys = [kp[3, 0, 0], kp[3, 0, 1], kp[0, 0, 0], kp[0, 0, 1], kp[2, 0, 0]]
+    vals = [vp[3, 0, 0], vp[3, 0, 1], vp[0, 0, 0], vp[0, 0, 1], vp[2, 0, 0]]
+    s = [0.9 * (q[0, 0, 0, 0] * kk[0] + q[0, 0, 0, 1] * kk[1]) for kk in keys]
+    w = [math.exp(x) for x in s]
+    z = sum(w)
+    want = [sum(w[i] * vals[i][c] for i in range(5)) / z for c in range(d)]
+    O, LSE = ar.ref_paged_decode(q, kp, vp, table, np.array([5]), 0.9)
+    np.testing.assert_allclose(O[0, 0, 0], want, rtol=1e-13)
+    assert LSE[0, 0, 0] == pytest.approx(math.log(z), rel=1e-14)
+
+
+def test_paged_decode_empty_sequence():
+    kp = _rand((2, 1, 4, 3), 57)
+    O, LSE = ar.ref_paged_decode(_rand((2, 1, 1, 3), 58), kp, kp, np.array([[0], [1]]), np.array([0, 3]), 1.0)
+    assert np.all(O[0] == 0) and LSE[0, 0, 0] == -np.inf
+    assert np.isfinite(LSE[1]).all()
+
+
+def test_mutant_paged_row_index_fails_dense_pin(monkeypatch):
+    """Swapping the block and the row index of a token must break the pin."""
+    def bad_gather(pool, block_table, seq_len, h):
+        pool = np.asarray(pool, dtype=np.float64)
+        bs = pool.shape[2]
+        rows = [pool[int(block_table[t % len(block_table)]), h, (t // len(block_table)) % bs] for t in range(seq_len)]
+        return np.array(rows).reshape(seq_len, pool.shape[3])
+
+    monkeypatch.setattr(ar, "gather_paged_rows", bad_gather)
+    with pytest.raises(AssertionError):
+        test_paged_decode_equals_dense_on_truncated_cache(4)
+
+
+# ---------------------------------------------------------------------------
 # Mutation tests: plausible oracle mistakes must fail the pins above
 # ---------------------------------------------------------------------------
 
