@@ -7,6 +7,9 @@ inputs:
     [16, 32, 32768, 128] in 256 chunks (map + merge)
   * backward, bf16 [2, 16, 4096, 64], causal (preprocess + dK/dV + dQ)
   * forward, bf16 [2, 32, 8192, 128], causal, inputs x 0.5 (reported only)
+  * split-K decode over a paged cache holding the same K/V cache in 16-token
+    blocks scattered over the pool by a random block table (reported only;
+    its output must equal the dense decode's bit for bit)
 
 `value` is the forward's TFLOP/s (4*B*H*N^2*d per call) from HIP events
 around its launch on the launch stream, averaged over the timed steps.
@@ -31,6 +34,7 @@ METRIC = "attn fwd TFLOP/s + % bf16 MFMA peak (B4 H16 N2048 d64); decode HBM GB/
 FWD = dict(B=4, H=16, N=2048, d=64, causal=False, input_scale=1.0)
 FWD_LONG = dict(B=2, H=32, N=8192, d=128, causal=True, input_scale=0.5)
 DEC = dict(B=16, H=32, L=32768, d=128, S=256)
+DEC_PAGED = dict(DEC, block_size=16)
 BWD = dict(B=2, H=16, N=4096, d=64, causal=True)
 
 
@@ -49,6 +53,11 @@ def dec_bytes(c):
     # K and V caches read once, q read and O written (bf16), LSE written (fp32)
     bh = c["B"] * c["H"]
     return 2 * bh * c["L"] * c["d"] * 2 + 2 * bh * c["d"] * 2 + bh * 4
+
+
+def dec_paged_bytes(c):
+    # the dense decode's bytes plus one int32 block id per block and the lengths
+    return dec_bytes(c) + c["B"] * (-(-c["L"] // c["block_size"])) * 4 + c["B"] * 4
 
 
 def _src_sha(*names):
@@ -121,12 +130,13 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--only", default="",
-                    help="comma-separated subset of fwd,decode,bwd,fwd_long to run (profiling passes)")
+                    help="comma-separated subset of fwd,decode,bwd,fwd_long,decode_paged to run "
+                         "(profiling passes)")
     a = ap.parse_args()
-    parts = ["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long"])
+    parts = ["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long"]) + ["decode_paged"]
     if a.only:
         parts = [p for p in a.only.split(",") if p]
-        bad = [p for p in parts if p not in ("fwd", "decode", "bwd", "fwd_long")]
+        bad = [p for p in parts if p not in ("fwd", "decode", "bwd", "fwd_long", "decode_paged")]
         if bad:
             ap.error(f"unknown --only parts {bad}")
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -136,9 +146,9 @@ def main():
 
     import torch
 
-    from exact_attention_05_amd import attn_bwd, attn_fwd, attn_fwd_splitk_decode
+    from exact_attention_05_amd import attn_bwd, attn_fwd, attn_fwd_splitk_decode, attn_fwd_splitk_decode_paged
     from exact_attention_05_amd.binding import attn_bwd_workspace_bytes, attn_decode_workspace_bytes
-    from exact_attention_05_amd.inputs import make_tensor
+    from exact_attention_05_amd.inputs import make_block_table, make_tensor
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -153,7 +163,7 @@ def main():
         fq, fk, fv = mk(0, ("q", "k", "v"), c["B"], c["H"], c["N"], c["d"])
         fo = torch.empty_like(fq)
         flse = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device=dev)
-    if "decode" in parts:
+    if "decode" in parts or "decode_paged" in parts:
         c = DEC
         dq_ = make_tensor(0, "q", c["B"], c["H"], 1, c["d"], bf16, device=dev)
         dk_, dv_ = mk(0, ("k", "v"), c["B"], c["H"], c["L"], c["d"])
@@ -161,6 +171,27 @@ def main():
         dlse = torch.empty((c["B"], c["H"]), dtype=torch.float32, device=dev)
         dws = torch.empty(attn_decode_workspace_bytes(c["B"], c["H"], c["d"], c["S"]) // 4,
                           dtype=torch.float32, device=dev)
+    if "decode_paged" in parts:
+        c = DEC_PAGED
+        bs = c["block_size"]
+        mb = c["L"] // bs
+        nb = c["B"] * mb
+        ptab = make_block_table(0, c["B"], mb, nb).to(dev)
+        # the dense cache's blocks placed at the pool slots the table names
+        slots = ptab.reshape(-1).long()
+
+        def to_pool(x):
+            pool = torch.empty((nb, c["H"], bs, c["d"]), dtype=bf16, device=dev)
+            pool[slots] = x.reshape(c["B"], c["H"], mb, bs, c["d"]).transpose(1, 2).reshape(nb, c["H"], bs, c["d"])
+            return pool
+
+        pk, pv = to_pool(dk_), to_pool(dv_)
+        plens = torch.full((c["B"],), c["L"], dtype=torch.int32, device=dev)
+        po = torch.empty_like(dq_)
+        plse = torch.empty_like(dlse)
+        pws = torch.empty_like(dws)
+        if "decode" not in parts:
+            del dk_, dv_
     if "bwd" in parts:
         c = BWD
         bq, bk, bv, bdo = mk(0, ("q", "k", "v", "do"), c["B"], c["H"], c["N"], c["d"])
@@ -203,6 +234,10 @@ def main():
             ev["fwd_long"][0].record(stream)
             attn_fwd(lq, lk, lv, causal=True, out=lo, lse=llse)
             ev["fwd_long"][1].record(stream)
+        if "decode_paged" in names:
+            ev["decode_paged"][0].record(stream)
+            attn_fwd_splitk_decode_paged(dq_, pk, pv, ptab, plens, DEC["S"], out=po, lse=plse, workspace=pws)
+            ev["decode_paged"][1].record(stream)
 
     def new_events():
         return {n: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for n in names}
@@ -248,7 +283,8 @@ def main():
         "config": {
             "workload": "attention forward bf16 [B=4,H=16,N=2048,d=64] non-causal (headline); split-K decode "
                         "bf16 q[16,32,1,128] x KV[16,32,32768,128], 256 chunks; backward bf16 [2,16,4096,64] "
-                        "causal; forward bf16 [2,32,8192,128] causal (reported)",
+                        "causal; forward bf16 [2,32,8192,128] causal (reported); the same decode over a "
+                        "paged cache of 16-token blocks (reported)",
             "global_batch": FWD["B"],
             "seq_len": FWD["N"],
             "parallelism": "single GPU",
@@ -287,6 +323,21 @@ def main():
         lt = fwd_flops(FWD_LONG) / (ms["fwd_long"] * 1e-3) / 1e12
         out["fwd_long_causal_tflops"] = round(lt, 3)
         out["fwd_long_causal_us"] = round(ms["fwd_long"] * 1e3, 2)
+    if "decode_paged" in ms:
+        pg = rate("decode_paged", dec_paged_bytes(DEC_PAGED), 1e9)
+        out["decode_paged_gbps"] = round(pg, 1)
+        out["decode_paged_pct_hbm"] = round(100.0 * pg / PEAK_HBM_GBPS, 2)
+        out["decode_paged_us"] = round(ms["decode_paged"] * 1e3, 2)
+        if "decode" in ms:
+            out["decode_paged_equals_dense"] = bool(torch.equal(po, do_) and torch.equal(plse, dlse))
+        out["roofline_decode_paged"] = {
+            "bound": "hbm",
+            "achieved": round(pg, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(pg / PEAK_HBM_GBPS, 4),
+            "traffic": _traffic("decode_paged_d128", ["decode.hip", "common.h"]),
+        }
     if not a.no_cpu_baseline and "fwd" in names:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline()

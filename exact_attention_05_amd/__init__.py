@@ -1,5 +1,5 @@
-"""MI355X-native exact attention: FA-2 style forward, split-K decode and
-recomputation backward, as hand-written HIP kernels for gfx950 behind a
+"""MI355X-native exact attention: FA-2 style forward, split-K decode (over a
+dense or a paged cache) and recomputation backward, as hand-written HIP kernels for gfx950 behind a
 C ABI (``libattn.so``, declared in ``include/attn.h``).
 
 The Python names mirror the C entry points; the shared library is loaded on
@@ -9,6 +9,7 @@ first use, and every call fails loudly when it is missing.
 __all__ = [
     "attn_fwd",
     "attn_fwd_splitk_decode",
+    "attn_fwd_splitk_decode_paged",
     "attn_bwd",
     "attn_decode_workspace_bytes",
     "attn_bwd_workspace_bytes",

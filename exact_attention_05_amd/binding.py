@@ -60,6 +60,9 @@ def _load():
     lib.attn_decode_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.attn_fwd_splitk_decode.restype = ci
     lib.attn_fwd_splitk_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, cf, vp]
+    lib.attn_fwd_splitk_decode_paged.restype = ci
+    lib.attn_fwd_splitk_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, ci,
+                                                 ci, cf, vp]
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci]
     lib.attn_bwd.restype = ci
@@ -161,6 +164,48 @@ def attn_fwd_splitk_decode(q, k_cache, v_cache, num_splits, scale=None, out=None
                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
                                         B, H, L, d, int(num_splits), _dtype_code(q), scale, _stream(dev))
     _check(st, "attn_fwd_splitk_decode")
+    return out, lse, workspace
+
+
+def attn_fwd_splitk_decode_paged(q, k_pool, v_pool, block_table, seq_lens, num_splits, scale=None, out=None,
+                                 lse=None, workspace=None):
+    """Split-K decode over a paged cache.
+
+    q [B, H, 1, d]; k_pool, v_pool [num_blocks, H, block_size, d];
+    block_table [B, max_blocks] int32 and seq_lens [B] int32 on the same GPU:
+    token t of sequence b is row t % block_size of pool block
+    block_table[b, t // block_size].  Returns (o [B, H, 1, d], lse [B, H],
+    workspace) with the workspace laid out as for attn_fwd_splitk_decode.
+    """
+    B, H, one, d = q.shape
+    _require(one == 1, "q must be [B, H, 1, d]")
+    _require(k_pool.dim() == 4, "k_pool must be [num_blocks, H, block_size, d]")
+    num_blocks, _, block_size, _ = k_pool.shape
+    dev = q.device
+    _check_bhnd("q", q, (B, H, 1, d), q.dtype, dev)
+    _check_bhnd("k_pool", k_pool, (num_blocks, H, block_size, d), q.dtype, dev)
+    _check_bhnd("v_pool", v_pool, (num_blocks, H, block_size, d), q.dtype, dev)
+    _require(block_table.dim() == 2 and block_table.shape[0] == B, "block_table must be [B, max_blocks]")
+    max_blocks = block_table.shape[1]
+    _check_bhnd("block_table", block_table, (B, max_blocks), torch.int32, dev)
+    _check_bhnd("seq_lens", seq_lens, (B,), torch.int32, dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    need = attn_decode_workspace_bytes(B, H, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty((max(need, 4) + 3) // 4, dtype=torch.float32, device=dev)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_bhnd("out", out, (B, H, 1, d), q.dtype, dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    else:
+        _check_bhnd("lse", lse, (B, H), torch.float32, dev)
+    st = _load().attn_fwd_splitk_decode_paged(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), _ptr(block_table), _ptr(seq_lens), _ptr(out), _ptr(lse),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), B, H, d, num_blocks, block_size,
+        max_blocks, int(num_splits), _dtype_code(q), scale, _stream(dev))
+    _check(st, "attn_fwd_splitk_decode_paged")
     return out, lse, workspace
 
 

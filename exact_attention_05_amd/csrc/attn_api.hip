@@ -73,7 +73,7 @@ size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits) {
 attn_status attn_fwd_splitk_decode(const void* q, const void* k_cache, const void* v_cache, void* o, float* lse,
                                    void* workspace, size_t workspace_bytes, int B, int H, int L, int d,
                                    int num_splits, attn_dtype dtype, float scale, void* stream) {
-  if (B < 1 || H < 1 || L < 1 || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (B < 1 || H < 1 || L < 1 || L > (1 << 30) || d < 1) return ATTN_ERR_INVALID_ARG;
   if (num_splits < 1 || num_splits > 65535) return ATTN_ERR_INVALID_ARG;
   if ((int64_t)B * H * num_splits > INT32_MAX) return ATTN_ERR_INVALID_ARG;
   if (!good_scale(scale)) return ATTN_ERR_INVALID_ARG;
@@ -85,6 +85,32 @@ attn_status attn_fwd_splitk_decode(const void* q, const void* k_cache, const voi
   if (workspace_bytes < attn_decode_workspace_bytes(B, H, d, num_splits)) return ATTN_ERR_WORKSPACE;
   attn::DecodeArgs a{q, k_cache, v_cache, o, lse, static_cast<float*>(workspace), B, H, L, d, num_splits, scale};
   return from_hip(attn::launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_fwd_splitk_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                                         const int* block_table, const int* seq_lens, void* o, float* lse,
+                                         void* workspace, size_t workspace_bytes, int B, int H, int d,
+                                         int num_blocks, int block_size, int max_blocks_per_seq, int num_splits,
+                                         attn_dtype dtype, float scale, void* stream) {
+  if (B < 1 || H < 1 || d < 1 || num_blocks < 1 || max_blocks_per_seq < 1) return ATTN_ERR_INVALID_ARG;
+  if (block_size < 1 || (block_size & (block_size - 1)) != 0) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)max_blocks_per_seq * block_size > (1 << 30)) return ATTN_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > 65535) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * H * num_splits > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  if (!good_scale(scale)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (!tensor_ok(q) || !tensor_ok(k_pool) || !tensor_ok(v_pool) || !tensor_ok(o)) return ATTN_ERR_INVALID_ARG;
+  if (block_table == nullptr || !aligned(block_table, 4) || seq_lens == nullptr || !aligned(seq_lens, 4))
+    return ATTN_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
+  if (!(dtype == ATTN_BF16 && (d == 64 || d == 128))) return ATTN_ERR_UNSUPPORTED;
+  if (workspace == nullptr || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < attn_decode_workspace_bytes(B, H, d, num_splits)) return ATTN_ERR_WORKSPACE;
+  int log2_bs = 0;
+  while ((1 << log2_bs) < block_size) ++log2_bs;
+  attn::DecodeArgs a{q, k_pool, v_pool, o, lse, static_cast<float*>(workspace), B, H, 0, d, num_splits, scale};
+  attn::PagedArgs p{block_table, seq_lens, max_blocks_per_seq, num_blocks, log2_bs};
+  return from_hip(attn::launch_decode_paged_bf16(a, p, static_cast<hipStream_t>(stream)));
 }
 
 size_t attn_bwd_workspace_bytes(int B, int H, int N) {

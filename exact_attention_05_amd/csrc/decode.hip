@@ -11,6 +11,9 @@
 // with the partial-state merge, and the chunk's (U, m, l) is written to the
 // workspace.  This is HBM-bandwidth work: no MFMA (a single query row).
 //
+// Paged variant: the same kernels, with each key's row found through a block
+// table (see PagedKV); the block ids of a round are fetched one round ahead.
+//
 // Reduce step (decode_merge_kernel): one workgroup per (b, h) merges its S
 // partials: m = max m_c, l = sum e^(m_c - m) l_c, U = sum e^(m_c - m) U_c,
 // O = U / l, LSE = m + ln l.
@@ -61,31 +64,76 @@ __device__ __forceinline__ float dot8_bf16(const u32x4& a, const u32x4& b) {
   return acc;
 }
 
-template <int D>
+// Where the keys of one (b, h) live.  Dense: row t of the [L, D] slab of
+// (b, h).  Paged: row t & (bs - 1) of pool block table[b][t >> log2 bs] of
+// head h, the pool laid out [num_blocks][H][bs][D] (the paged block table
+// that "FlashAttention 1 和 FlashAttention 2 的区别", section 13, names as a
+// KV-cache layout of decode kernels).
+struct PagedKV {
+  const int32_t* table;    // [B][max_blocks]
+  const int32_t* seq_lens; // [B]
+  int H, max_blocks, num_blocks, log2_bs;
+};
+
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const __bf16* __restrict__ Q,
                                                                   const __bf16* __restrict__ K,
                                                                   const __bf16* __restrict__ V,
                                                                   float* __restrict__ ws, int L, int S,
-                                                                  int BH, float scale_log2) {
+                                                                  int BH, float scale_log2, PagedKV pg) {
   constexpr int LPK = D / 8;       // lanes per key (8 bf16 each)
   constexpr int SPW = 64 / LPK;    // key slots per wavefront
   constexpr int NS = SPW * kWaves; // key slots per workgroup
+  constexpr int STEP = NS * kRound;
   __shared__ float sm_u[kWaves][D];
   __shared__ float sm_ml[kWaves][2];
 
-  const int id = blockIdx.x;
-  const int bh = id / S;
-  const int c = id % S;
-  const int lo = (int)(((int64_t)c * L) / S);
-  const int hi = (int)(((int64_t)(c + 1) * L) / S);
-
+  // Work order.  Each XCD takes a contiguous range of the work (xcd_remap).
+  // Dense: the chunks of one (b, h) are consecutive, so the workgroups in
+  // flight stream a few contiguous [L, D] slabs.  Paged: the heads of one
+  // chunk are consecutive instead; the pool is block-major, so the H heads of
+  // a block are adjacent and an in-order table is read as contiguous runs
+  // (head-major order would stride the pool by H blocks and load a few
+  // memory channels far more than the rest).
+  const int id = xcd_remap(blockIdx.x, BH * S);
+  const int bh = PAGED ? id % BH : id / S;
+  const int c = PAGED ? id / BH : id % S;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int u = lane % LPK;                    // d chunk: dims 8u .. 8u+7
   const int slot = wave * SPW + lane / LPK;    // key slot in the workgroup
 
-  const __bf16* Kh = K + (int64_t)bh * L * D;
-  const __bf16* Vh = V + (int64_t)bh * L * D;
+  // Paged: the sequence length comes from seq_lens, clamped to what the
+  // table can address, so a bad length or block id never reads outside the
+  // pool (the result is then unspecified, not a fault).
+  const int32_t* tab = nullptr;
+  int h = 0;
+  if constexpr (PAGED) {
+    const int b = bh / pg.H;
+    h = bh - b * pg.H;
+    tab = pg.table + (int64_t)b * pg.max_blocks;
+    L = min(max(pg.seq_lens[b], 0), pg.max_blocks << pg.log2_bs);
+  }
+  const int lo = (int)(((int64_t)c * L) / S);
+  const int hi = (int)(((int64_t)(c + 1) * L) / S);
+  const int bs_mask = (1 << pg.log2_bs) - 1;
+
+  // pool block of each of this lane's keys in the round at k0
+  auto fetch_blocks = [&](int k0, int (&blk)[kRound]) {
+#pragma unroll
+    for (int r = 0; r < kRound; ++r) {
+      const int key = k0 + r * NS + slot;
+      blk[r] = key < hi ? min(max(tab[key >> pg.log2_bs], 0), pg.num_blocks - 1) : 0;
+    }
+  };
+  // element offset of dims 8u.. of key `key` (in block blk when paged)
+  auto row_off = [&](int key, int blk) -> int64_t {
+    if constexpr (PAGED)
+      return ((((int64_t)blk * pg.H + h) << pg.log2_bs) + (key & bs_mask)) * D + 8 * u;
+    else
+      return ((int64_t)bh * L + key) * D + 8 * u;
+  };
+
   const u32x4 qv = *reinterpret_cast<const u32x4*>(Q + (int64_t)bh * D + 8 * u);
 
   State st;
@@ -94,16 +142,22 @@ __global__ __launch_bounds__(kThreads) void decode_partial_kernel(const __bf16* 
 #pragma unroll
   for (int e = 0; e < 8; ++e) st.u[e] = 0.f;
 
-  for (int k0 = lo; k0 < hi; k0 += NS * kRound) {
+  int blk[kRound] = {};
+  if constexpr (PAGED) fetch_blocks(lo, blk);
+  for (int k0 = lo; k0 < hi; k0 += STEP) {
     u32x4 kr[kRound], vr[kRound];
 #pragma unroll
     for (int r = 0; r < kRound; ++r) {
       const int key = k0 + r * NS + slot;
       const bool ok = key < hi;
+      const int64_t off = row_off(key, blk[r]);
       // the cache is streamed once: non-temporal loads keep it out of the caches
-      kr[r] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Kh + (int64_t)key * D + 8 * u)) : u32x4{};
-      vr[r] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Vh + (int64_t)key * D + 8 * u)) : u32x4{};
+      kr[r] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(K + off)) : u32x4{};
+      vr[r] = ok ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(V + off)) : u32x4{};
     }
+    // block ids of the next round, issued after this round's loads so their
+    // latency hides behind this round's arithmetic
+    if constexpr (PAGED) fetch_blocks(k0 + STEP, blk);
     float s[kRound];
     float rmax = kNegInf;
 #pragma unroll
@@ -249,13 +303,13 @@ __global__ __launch_bounds__(kThreads) void decode_merge_kernel(const float* __r
   }
 }
 
-template <int D>
-hipError_t run_decode(const DecodeArgs& a, hipStream_t s) {
+template <int D, bool PAGED>
+hipError_t run_decode(const DecodeArgs& a, const PagedKV& pg, hipStream_t s) {
   const int BH = a.B * a.H;
   const int64_t nwg = (int64_t)BH * a.splits;
-  hipLaunchKernelGGL((decode_partial_kernel<D>), dim3((unsigned)nwg), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((decode_partial_kernel<D, PAGED>), dim3((unsigned)nwg), dim3(kThreads), 0, s,
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                     static_cast<const __bf16*>(a.v), a.ws, a.L, a.splits, BH, a.scale * kLog2e);
+                     static_cast<const __bf16*>(a.v), a.ws, a.L, a.splits, BH, a.scale * kLog2e, pg);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((decode_merge_kernel<D>), dim3(BH), dim3(kThreads), 0, s, a.ws, static_cast<__bf16*>(a.o),
@@ -266,7 +320,13 @@ hipError_t run_decode(const DecodeArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
-  return a.d == 64 ? run_decode<64>(a, s) : run_decode<128>(a, s);
+  const PagedKV none{nullptr, nullptr, a.H, 0, 0, 0};
+  return a.d == 64 ? run_decode<64, false>(a, none, s) : run_decode<128, false>(a, none, s);
+}
+
+hipError_t launch_decode_paged_bf16(const DecodeArgs& a, const PagedArgs& p, hipStream_t s) {
+  const PagedKV pg{p.block_table, p.seq_lens, a.H, p.max_blocks, p.num_blocks, p.log2_bs};
+  return a.d == 64 ? run_decode<64, true>(a, pg, s) : run_decode<128, true>(a, pg, s);
 }
 
 }  // namespace attn

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <stdint.h>
 
 namespace attn {
 
@@ -33,6 +34,15 @@ struct DecodeArgs {
 };
 
 hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s);
+
+// Paged K/V cache: DecodeArgs.k/.v are the block pools, DecodeArgs.L unused.
+struct PagedArgs {
+  const int32_t* block_table;  // [B][max_blocks]
+  const int32_t* seq_lens;     // [B]
+  int max_blocks, num_blocks, log2_bs;
+};
+
+hipError_t launch_decode_paged_bf16(const DecodeArgs& a, const PagedArgs& p, hipStream_t s);
 
 struct BwdArgs {
   const void* q;

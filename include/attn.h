@@ -1,7 +1,7 @@
 /*
  * attn.h -- C ABI of libattn.so: exact attention on AMD MI355X (gfx950).
  *
- * Three operations, each an FA-2 style tiled computation that never writes
+ * Four entry points, each an FA-2 style tiled computation that never writes
  * the N x N score or probability matrix to device memory:
  *
  *   attn_fwd                O = softmax(scale * Q K^T) V and the per-row
@@ -9,6 +9,9 @@
  *   attn_fwd_splitk_decode  the same for a single query row against a long
  *                           key/value cache, split into chunks whose partial
  *                           (U, m, l) states are merged afterwards.
+ *   attn_fwd_splitk_decode_paged
+ *                           the same decode over a paged cache addressed
+ *                           through a per-sequence block table.
  *   attn_bwd                dQ, dK, dV by recomputing P from the saved LSE.
  *
  * Conventions for every entry point:
@@ -113,7 +116,7 @@ size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits);
  *              completes) it holds the partials, fp32, in this order:
  *              U [B, H, S, d], then m [B, H, S] (natural-log units of the
  *              scaled score), then l [B, H, S].
- *   num_splits: 1 <= S <= 65535.
+ *   num_splits: 1 <= S <= 65535;  L <= 2^30.
  *
  * Supported: ATTN_BF16 with d in {64, 128}.
  * Errors as attn_fwd, plus ATTN_ERR_WORKSPACE for a NULL or short workspace.
@@ -122,6 +125,48 @@ attn_status attn_fwd_splitk_decode(const void* q, const void* k_cache, const voi
                                    void* o, float* lse, void* workspace, size_t workspace_bytes,
                                    int B, int H, int L, int d, int num_splits, attn_dtype dtype,
                                    float scale, void* stream);
+
+/*
+ * attn_fwd_splitk_decode_paged -- the split-K decode of
+ * attn_fwd_splitk_decode over a paged key/value cache.
+ *
+ * "FlashAttention 1 和 FlashAttention 2 的区别", section 13, names the paged
+ * block table as a KV-cache layout that decode kernels are tuned for; the
+ * layout is fixed here as follows.  The cache is a pool of `num_blocks`
+ * blocks of `block_size` token rows per head; sequence b has
+ * seq_lens[b] tokens, and its token t is row (t mod block_size) of pool block
+ * block_table[b][t / block_size].  For every (b, h) the result is that of
+ * attn_fwd_splitk_decode on the gathered cache of length L_b = seq_lens[b]:
+ * chunk c covers tokens [floor(c*L_b/S), floor((c+1)*L_b/S)), and the chunk
+ * partials are merged as described there.  A sequence with L_b = 0 gives
+ * O = 0 and LSE = -inf.
+ *
+ *   q          : [B, H, 1, d] in `dtype`
+ *   k_pool     : [num_blocks, H, block_size, d] in `dtype`;  v_pool likewise
+ *   block_table: [B, max_blocks_per_seq] int32, DEVICE memory; entries past
+ *                ceil(L_b / block_size) are not read
+ *   seq_lens   : [B] int32, DEVICE memory
+ *   o, lse, workspace, num_splits: as attn_fwd_splitk_decode (the workspace
+ *                size is attn_decode_workspace_bytes(B, H, d, num_splits))
+ *   block_size : a power of two, 1 <= block_size;
+ *                max_blocks_per_seq * block_size <= 2^30
+ *
+ * The device-side values are not validated on the host (they are never
+ * read there): a length outside [0, max_blocks_per_seq * block_size] is
+ * clamped into it and a block id outside [0, num_blocks) is clamped into
+ * it, so no access leaves the pool, but the result is then unspecified.
+ *
+ * Supported: ATTN_BF16 with d in {64, 128}.
+ * Errors as attn_fwd_splitk_decode; ATTN_ERR_INVALID_ARG also for a NULL or
+ * 4-byte-misaligned block_table or seq_lens, num_blocks < 1,
+ * max_blocks_per_seq < 1 or a block_size that is not a power of two.
+ */
+attn_status attn_fwd_splitk_decode_paged(const void* q, const void* k_pool, const void* v_pool,
+                                         const int* block_table, const int* seq_lens, void* o,
+                                         float* lse, void* workspace, size_t workspace_bytes, int B,
+                                         int H, int d, int num_blocks, int block_size,
+                                         int max_blocks_per_seq, int num_splits, attn_dtype dtype,
+                                         float scale, void* stream);
 
 /*
  * Workspace size in bytes that attn_bwd needs: 24 bytes per query row

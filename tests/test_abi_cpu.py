@@ -29,7 +29,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("attn_fwd", "attn_fwd_splitk_decode", "attn_bwd", "attn_decode_workspace_bytes",
+    for n in ("attn_fwd", "attn_fwd_splitk_decode", "attn_fwd_splitk_decode_paged", "attn_bwd",
+              "attn_decode_workspace_bytes",
               "attn_bwd_workspace_bytes", "attn_status_string", "attn_abi_version"):
         assert n in names
 
@@ -107,6 +108,7 @@ def test_decode_validation():
     assert call(q=NULL) == INVALID
     assert call(k=MIS) == INVALID
     assert call(L=0) == INVALID
+    assert call(L=(1 << 30) + 1) == INVALID
     assert call(S=0) == INVALID
     assert call(S=65536) == INVALID
     assert call(sc=-1.0) == INVALID
@@ -114,6 +116,40 @@ def test_decode_validation():
     assert call(dt=F32) == UNSUPPORTED
     assert call(ws=NULL) == WORKSPACE
     assert call(ws=MIS) == WORKSPACE
+    assert call(wsb=ws_need - 1) == WORKSPACE
+
+
+def test_paged_decode_validation():
+    lib = _lib()
+    f = lib.attn_fwd_splitk_decode_paged
+    ws_need = lib.attn_decode_workspace_bytes(2, 2, 128, 4)
+    I4 = ctypes.c_void_p(0x10004)  # 4-byte aligned: enough for the int32 table and lengths
+    base = dict(q=P, k=P, v=P, tab=I4, lens=I4, o=P, lse=NULL, ws=P, wsb=ws_need, B=2, H=2, d=128, nb=10, bs=16,
+                mb=8, S=4, dt=BF16, sc=0.1)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["q"], a["k"], a["v"], a["tab"], a["lens"], a["o"], a["lse"], a["ws"], a["wsb"], a["B"], a["H"],
+                 a["d"], a["nb"], a["bs"], a["mb"], a["S"], a["dt"], a["sc"], None)
+
+    assert call(q=NULL) == INVALID
+    assert call(v=MIS) == INVALID
+    assert call(tab=NULL) == INVALID
+    assert call(lens=NULL) == INVALID
+    assert call(tab=ctypes.c_void_p(0x10002)) == INVALID
+    assert call(lens=ctypes.c_void_p(0x10001)) == INVALID
+    assert call(B=0) == INVALID
+    assert call(nb=0) == INVALID
+    assert call(mb=0) == INVALID
+    for bs in (0, -16, 3, 24, 48):
+        assert call(bs=bs) == INVALID, bs
+    assert call(bs=1 << 20, mb=(1 << 10) + 1) == INVALID
+    assert call(S=0) == INVALID
+    assert call(S=65536) == INVALID
+    assert call(sc=float("nan")) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(d=64, dt=F32) == UNSUPPORTED
+    assert call(ws=NULL) == WORKSPACE
     assert call(wsb=ws_need - 1) == WORKSPACE
 
 
