@@ -19,7 +19,9 @@ Sources (web pages, cited by title and section):
 * [operatorworld] "FlashAttention tiling" (operatorworld.com): the online
   softmax update equations and degeneration checks; backward by recomputation.
 * [Triton-ch8] "8. FlashAttention 实战" (triton-tutorial.pages.dev):
-  section 8.1 (naive attention), 8.3 (online softmax), 8.8 (backward).
+  section 8.1 (naive attention), 8.3 (online softmax), 8.8 (backward),
+  8.9 (FP8 attention: block quantisation, P requantised to FP8,
+  incoherent processing).
 
 Every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle_pins.py`` against values or properties the pages and the
@@ -40,4 +42,9 @@ from .attention_ref import (  # noqa: F401
     decode_chunk_bounds,
     gather_paged_rows,
     ref_paged_decode,
+    e4m3_round,
+    pow2_block_scale,
+    hadamard_rotate,
+    quantize_fp8_blocks,
+    ref_fwd_fp8,
 )

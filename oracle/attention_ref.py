@@ -312,3 +312,136 @@ def ref_paged_decode(q, k_pool, v_pool, block_table, seq_lens, scale):
             O[b, h], LSE[b, h] = ref_fwd(q[b, h], kb, vb, scale)
     return O, LSE
 
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) forward ([Triton-ch8] section 8.9)
+# ---------------------------------------------------------------------------
+
+E4M3_MAX = 448.0
+P_EXP = 3  # P~ is quantised as e4m3(2^(u - M + P_EXP) * r), see ref_fwd_fp8
+
+
+def e4m3_round(x):
+    """Round to the nearest FP8 E4M3 value, ties to even, for |x| <= 448.
+
+    The format ([Triton-ch8] section 8.9.1: 4 exponent bits, 3 mantissa
+    bits, largest finite value 448): exponent bias 7, normal values
+    (1 + m/8) 2^(e-7) for e = 1..15, subnormals (m/8) 2^-6, so the spacing is
+    2^(e-3) for a value in [2^e, 2^(e+1)) and 2^-9 below 2^-6.
+    """
+    x = _f64(x)
+    a = np.abs(x)
+    assert np.all(a <= E4M3_MAX), "e4m3_round expects clamped input"
+    _, ex = np.frexp(a)                      # a = f 2^ex, f in [0.5, 1)
+    e = np.maximum(ex - 1, -6)               # floor(log2 a), subnormal range at -6
+    ulp = np.ldexp(1.0, e - 3)
+    return np.sign(x) * np.round(a / ulp) * ulp   # a / ulp is exact; np.round ties to even
+
+
+def hadamard_rotate(x, signs):
+    """Incoherent processing ([Triton-ch8] section 8.9.5): x' = x D H / sqrt(d)
+    with D = diag(signs) (random +-1, drawn by the caller) and H the Sylvester
+    Hadamard matrix of order d (a power of two).  D H / sqrt(d) is
+    orthogonal, so x' y'^T = x y^T."""
+    x = _f64(x)
+    d = x.shape[-1]
+    H = np.array([[1.0]])
+    while H.shape[0] < d:
+        H = np.block([[H, H], [H, -H]])
+    assert H.shape[0] == d, "d must be a power of two"
+    return (x * _f64(signs)) @ H / np.sqrt(d)
+
+
+def pow2_block_scale(amax):
+    """The block scale: the smallest power of two 2^k with 448 2^k >= amax
+    (1 for an all-zero block), so amax / scale lies in (224, 448].  The
+    page takes scale = max|x| / 448 ([Triton-ch8] section 8.9.4); a power of
+    two keeps x / scale exact and lets the matrix unit apply the scale.  The
+    exponent is kept in [-126, 127] (normal fp32 numbers), so blocks with
+    amax < 448 2^-126 use fewer than the top binade."""
+    amax = float(amax)
+    if amax == 0.0:
+        return 1.0
+    k = int(np.ceil(np.log2(amax / E4M3_MAX)))
+    while E4M3_MAX * 2.0 ** (k - 1) >= amax:     # exact comparisons fix a misrounded log
+        k -= 1
+    while E4M3_MAX * 2.0 ** k < amax:
+        k += 1
+    return 2.0 ** max(k, -126)
+
+
+def quantize_fp8_blocks(x, block_rows, signs=None):
+    """Per-block FP8 quantisation ([Triton-ch8] sections 8.9.3-8.9.4).
+
+    x: [..., N, d].  Rows are grouped into blocks of ``block_rows``; each
+    block gets scale = pow2_block_scale(max|x|) and codes
+    e4m3(clamp(x / scale, +-448)).  With ``signs`` the rows are first rotated
+    by hadamard_rotate and rounded to fp32 (the precision the values are
+    held in before the division).  Returns (values [..., N, d] float64 --
+    the e4m3 values, exactly --, scales [..., ceil(N / block_rows)]).
+    """
+    x = _f64(x)
+    if signs is not None:
+        x = hadamard_rotate(x, signs)
+    x32 = x.astype(np.float32).astype(np.float64)
+    N = x.shape[-2]
+    nb = -(-N // block_rows)
+    vals = np.zeros(x.shape)
+    scales = np.zeros(x.shape[:-2] + (nb,))
+    for idx in np.ndindex(*x.shape[:-2]):
+        for b in range(nb):
+            blk = x32[idx][b * block_rows:(b + 1) * block_rows]
+            s = pow2_block_scale(np.max(np.abs(blk)))
+            vals[idx][b * block_rows:(b + 1) * block_rows] = e4m3_round(np.clip(blk / s, -E4M3_MAX, E4M3_MAX))
+            scales[idx][b] = s
+    return vals, scales
+
+
+def _rows_of_blocks(scales, block_rows, N):
+    """Per-row copy of per-block scales: [..., nb] -> [..., N]."""
+    return np.repeat(_f64(scales), block_rows, axis=-1)[..., :N]
+
+
+def ref_fwd_fp8(q8, k8, v8, sq, sk, sv, scale, causal=False, block_m=128, block_n=64, ref_shift=0):
+    """FP8 attention forward ([Triton-ch8] section 8.9.3): FP8 products with
+    fp32 (here exact) accumulation, the softmax statistics in high precision,
+    P~ quantised to FP8 before the second product.
+
+    q8, k8, v8: [..., N, d] e4m3 values; sq: per-block Q scales
+    [..., ceil(N / block_m)]; sk, sv: per-block K and V scales
+    [..., ceil(N / block_n)] (dequantised value = e4m3 value x its block's
+    scale, section 8.9.4).  Per (b, h) and query row:
+
+        S   = scale (q8 sq) (k8 sk)^T        (masked if causal)
+        u   = S log2(e),   M = ceil(max_j u_j) + ref_shift   (an integer)
+        a_j = 2^(u_j - M + P_EXP),   l = sum_j a_j       (unquantised, as the
+                                                         page's fp32 l)
+        O   = sum_j e4m3(a_j) (v8_j sv_j) / l
+        LSE = (M + log2 l - P_EXP) ln 2
+
+    P~ is thus quantised with the fixed scale 2^-P_EXP relative to an
+    integer reference instead of the page's data-dependent per-block p scale.
+    Since e4m3(a 2^k) = 2^k e4m3(a) while both are normal numbers, every
+    integer reference gives the same O up to values in the subnormal range;
+    ``ref_shift`` exists to pin that.  Returns (O [..., N, d], LSE [..., N]).
+    """
+    q8, k8, v8 = _f64(q8), _f64(k8), _f64(v8)
+    N, Nk = q8.shape[-2], k8.shape[-2]
+    O = np.zeros(q8.shape[:-1] + (v8.shape[-1],))
+    LSE = np.full(q8.shape[:-1], NEG_INF)
+    for h in _heads(q8.shape):
+        qd = q8[h] * _rows_of_blocks(sq[h], block_m, N)[:, None]
+        kd = k8[h] * _rows_of_blocks(sk[h], block_n, Nk)[:, None]
+        vd = v8[h] * _rows_of_blocks(sv[h], block_n, Nk)[:, None]
+        u = _scores(qd, kd, scale, causal, np.arange(N)) * np.log2(np.e)
+        for i in range(N):
+            vis = np.isfinite(u[i])
+            if not vis.any():
+                continue
+            M = np.ceil(np.max(u[i][vis])) + ref_shift
+            a = np.where(vis, np.exp2(np.where(vis, u[i], 0.0) - M + P_EXP), 0.0)
+            l = a.sum()
+            O[h][i] = (e4m3_round(a) @ vd) / l
+            LSE[h][i] = (M + np.log2(l) - P_EXP) * np.log(2.0)
+    return O, LSE

@@ -437,6 +437,177 @@ def test_mutant_paged_row_index_fails_dense_pin(monkeypatch):
 
 
 # ---------------------------------------------------------------------------
+# FP8 (E4M3) quantisation and forward ([Triton-ch8] section 8.9)
+# ---------------------------------------------------------------------------
+
+def test_e4m3_round_matches_torch_cast():
+    """torch's float8_e4m3fn cast is an independent implementation of the
+    same rounding (nearest, ties to even) on [-448, 448]."""
+    rng = np.random.default_rng(60)
+    x = np.concatenate([
+        rng.standard_normal(20000) * 30,
+        np.exp2(rng.uniform(-14, 8.8, 20000)) * rng.choice([-1, 1], 20000),
+        # every midpoint between neighbouring positive e4m3 values
+        0.5 * (ar.e4m3_round(np.exp2(np.arange(-9, 8.8, 0.01))[:-1]) +
+               ar.e4m3_round(np.exp2(np.arange(-9, 8.8, 0.01))[1:])),
+    ])
+    x = np.clip(x, -448, 448)
+    ref = torch.tensor(x).to(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(ar.e4m3_round(x), ref)
+
+
+def test_e4m3_round_values_from_the_format():
+    # representable values map to themselves; ties go to the even mantissa
+    grid = [0.0, 2.0 ** -9, 3 * 2.0 ** -9, 2.0 ** -6, 1.0, 1.125, 1.75, 240.0, 448.0]
+    assert list(ar.e4m3_round(np.array(grid))) == grid
+    assert ar.e4m3_round(np.array([1.0625, 1.1875, 2.0 ** -10, 3 * 2.0 ** -10, 432.0])).tolist() == \
+        [1.0, 1.25, 0.0, 2.0 ** -8, 448.0]
+    assert ar.e4m3_round(np.array([-1.0625]))[0] == -1.0
+
+
+def test_pow2_block_scale():
+    for amax in (448.0, 449.0, 224.0, 224.5, 1.0, 3.5, 1e-3, 7e20):
+        s = ar.pow2_block_scale(amax)
+        assert math.log2(s) == int(math.log2(s))
+        assert 224.0 < amax / s <= 448.0, (amax, s)
+    assert ar.pow2_block_scale(0.0) == 1.0
+    assert ar.pow2_block_scale(1e-40) == 2.0 ** -126
+
+
+def test_quantize_fp8_blocks_known_block():
+    x = np.array([[1.0, -2.0, 0.5], [0.25, 0.0, 1.5]])
+    vals, scales = ar.quantize_fp8_blocks(x[None], 2)
+    # amax 2: 448 2^-8 = 1.75 < 2 <= 3.5 = 448 2^-7, so the scale is 2^-7
+    assert scales.tolist() == [[2.0 ** -7]]
+    assert vals[0].tolist() == [[128.0, -256.0, 64.0], [32.0, 0.0, 192.0]]
+
+
+def test_quantize_fp8_blocks_error_bound():
+    """Dequantised values are within half an e4m3 spacing of the input:
+    2^-4 relative in the normal range, 2^-10 x scale below it."""
+    x = np.random.default_rng(61).standard_normal((2, 300, 64)) * np.exp2(np.arange(300) % 7)[:, None]
+    vals, scales = ar.quantize_fp8_blocks(x, 64)
+    sr = np.repeat(scales, 64, axis=-1)[..., :300, None]
+    deq = vals * sr
+    bound = np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * sr)
+    assert np.all(np.abs(deq - x) <= bound)
+    assert np.all(np.abs(vals) <= 448)
+    blk_max = np.abs(vals[:, :256]).reshape(2, 4, 64 * 64).max(-1)  # the four full blocks
+    assert np.all((blk_max >= 224) & (blk_max <= 448))
+
+
+def test_hadamard_rotation_is_orthogonal():
+    from scipy.linalg import hadamard
+
+    d = 64
+    s = np.random.default_rng(62).choice([-1.0, 1.0], d)
+    x, y = _rand((5, d), 63), _rand((7, d), 64)
+    xr, yr = ar.hadamard_rotate(x, s), ar.hadamard_rotate(y, s)
+    np.testing.assert_allclose(xr @ yr.T, x @ y.T, rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(xr, (x * s) @ hadamard(d) / 8.0, rtol=1e-13, atol=1e-14)
+    e = np.zeros(d)
+    e[5] = 1.0
+    assert np.allclose(np.abs(ar.hadamard_rotate(e, s)), 1.0 / 8.0)
+
+
+def _fp8_inputs(N, d, seed, bm=128, bn=64, scale_rows=None):
+    q, k, v = (_rand((1, 1, N, d), seed + i) for i in range(3))
+    if scale_rows is not None:
+        v = v * scale_rows[None, None, :, None]
+    q8, sq = ar.quantize_fp8_blocks(q, bm)
+    k8, sk = ar.quantize_fp8_blocks(k, bn)
+    v8, sv = ar.quantize_fp8_blocks(v, bn)
+    return q8, k8, v8, sq, sk, sv
+
+
+def _dequant(x8, s, rows):
+    """e4m3 values times their block's scale (written out here, not taken
+    from the oracle, so the mutation test below changes one side only)."""
+    return x8 * np.repeat(s, rows, axis=-1)[..., :x8.shape[-2], None]
+
+
+def test_fp8_forward_uniform_scores_give_mean_of_v():
+    N = 200
+    q8, k8, v8, sq, sk, sv = _fp8_inputs(N, 64, 70)
+    O, LSE = ar.ref_fwd_fp8(0 * q8, k8, v8, sq, sk, sv, 0.125)
+    np.testing.assert_allclose(O[0, 0], _dequant(v8, sv, 64)[0, 0].mean(0)[None].repeat(N, 0), rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(LSE, math.log(N), rtol=1e-14)
+
+
+def test_fp8_forward_single_key():
+    """One key: O = v^ e4m3(a) / a with a = 2^(u - ceil(u) + 3)."""
+    q8, k8, v8, sq, sk, sv = _fp8_inputs(1, 64, 71)
+    u = 0.125 * float(_dequant(q8, sq, 128)[0, 0, 0] @ _dequant(k8, sk, 64)[0, 0, 0]) * math.log2(math.e)
+    a = 2.0 ** (u - math.ceil(u) + 3)
+    O, LSE = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125)
+    want = _dequant(v8, sv, 64)[0, 0, 0] * float(ar.e4m3_round(np.array([a]))[0]) / a
+    np.testing.assert_allclose(O[0, 0, 0], want, rtol=1e-13)
+    assert LSE[0, 0, 0] == pytest.approx(u * math.log(2), rel=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_forward_without_p_rounding_is_exact_attention(monkeypatch, causal):
+    """With P~ left unrounded the method is exact attention of the dequantised
+    inputs (section 8.9.4), so every step other than P~'s rounding is pinned
+    to the plain definition."""
+    q8, k8, v8, sq, sk, sv = _fp8_inputs(150, 64, 72, bm=32)
+    monkeypatch.setattr(ar, "e4m3_round", lambda x: np.asarray(x, dtype=np.float64))
+    O, LSE = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125, causal, block_m=32)
+    O2, L2 = ar.ref_fwd(_dequant(q8, sq, 32), _dequant(k8, sk, 64), _dequant(v8, sv, 64), 0.125, causal)
+    np.testing.assert_allclose(O, O2, rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(LSE, L2, rtol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_forward_error_within_p_rounding_bound(causal):
+    """O differs from exact attention of the dequantised inputs only by P~'s
+    rounding: |dO| <= sum_j |e4m3(a_j) - a_j| |v_j| / l <= (2^-4 + 2^-7) max|v|
+    (half a spacing: 2^-4 relative for normal a_j; subnormal a_j < 2^-6 are
+    off by at most 2^-10 each, and l >= 4 since M < max u + 1).  V's rows
+    vary in size so that a mix-up of V block scales breaks the bound."""
+    N = 256
+    q8, k8, v8, sq, sk, sv = _fp8_inputs(N, 64, 73, scale_rows=np.exp2(np.arange(N) // 64 * 3.0))
+    O, _ = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125, causal)
+    vd = _dequant(v8, sv, 64)
+    O2, _ = ar.ref_fwd(_dequant(q8, sq, 128), _dequant(k8, sk, 64), vd, 0.125, causal)
+    err = np.abs(O - O2)
+    assert err.max() <= (2.0 ** -4 + N * 2.0 ** -12) * np.abs(vd).max()
+    # and, on average, inside the per-key relative bound (errors of different keys partly cancel)
+    assert np.sqrt((err ** 2).mean()) <= 2.0 ** -4 * np.sqrt((O2 ** 2).mean())
+
+
+def test_fp8_forward_integer_reference_shift():
+    """Every integer reference gives the same O while the a_j stay normal."""
+    q8, k8, v8, sq, sk, sv = _fp8_inputs(120, 64, 74)
+    O0, L0 = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.05)
+    for shift in (1, 2, -3):
+        O1, L1 = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.05, ref_shift=shift)
+        np.testing.assert_allclose(O1, O0, rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(L1, L0, rtol=1e-13)
+
+
+def test_hadamard_rotation_helps_outlier_features():
+    """Incoherent processing ([Triton-ch8] section 8.9.5): with a few feature
+    dimensions far larger than the rest, rotating Q and K before the block
+    quantisation lowers the error of the scores."""
+    rng = np.random.default_rng(75)
+    N, d = 256, 64
+    q, k = rng.standard_normal((1, 1, N, d)), rng.standard_normal((1, 1, N, d))
+    q[..., 3] *= 40.0
+    k[..., 3] *= 40.0
+    s = rng.choice([-1.0, 1.0], d)
+    S = q[0, 0] @ k[0, 0].T
+
+    def score_err(signs):
+        q8, sq = ar.quantize_fp8_blocks(q, 64, signs)
+        k8, sk = ar.quantize_fp8_blocks(k, 64, signs)
+        Sq = _dequant(q8, sq, 64)[0, 0] @ _dequant(k8, sk, 64)[0, 0].T
+        return np.sqrt(((Sq - S) ** 2).mean())
+
+    assert score_err(s) < 0.5 * score_err(None)
+
+
+# ---------------------------------------------------------------------------
 # Mutation tests: plausible oracle mistakes must fail the pins above
 # ---------------------------------------------------------------------------
 
@@ -508,6 +679,19 @@ def test_mutant_merge_without_weights_fails_decode_pin(monkeypatch):
     O1, _ = ar.ref_fwd(q, k, v, 1.0, False)
     O2, _ = ar.ref_splitk_decode(q, k, v, 1.0, 4)
     assert np.max(np.abs(O2 - O1)) > 1e-3
+
+
+def test_mutant_fp8_v_scale_mixup_fails_bound(monkeypatch):
+    """Scaling V by the Q block scales instead of its own must break the
+    rounding bound pin."""
+    true_rows = ar._rows_of_blocks
+
+    def bad_rows(scales, block_rows, N):
+        return true_rows(scales, block_rows, N)[..., ::-1].copy()  # rows take another block's scale
+
+    monkeypatch.setattr(ar, "_rows_of_blocks", bad_rows)
+    with pytest.raises(AssertionError):
+        test_fp8_forward_error_within_p_rounding_bound(False)
 
 
 def test_oracle_exports():
