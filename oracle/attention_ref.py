@@ -403,7 +403,8 @@ def _rows_of_blocks(scales, block_rows, N):
     return np.repeat(_f64(scales), block_rows, axis=-1)[..., :N]
 
 
-def ref_fwd_fp8(q8, k8, v8, sq, sk, sv, scale, causal=False, block_m=128, block_n=64, ref_shift=0):
+def ref_fwd_fp8(q8, k8, v8, sq, sk, sv, scale, causal=False, block_m=128, block_n=64, ref_shift=0,
+                tie_rel=None, score_rel=0.0):
     """FP8 attention forward ([Triton-ch8] section 8.9.3): FP8 products with
     fp32 (here exact) accumulation, the softmax statistics in high precision,
     P~ quantised to FP8 before the second product.
@@ -425,11 +426,27 @@ def ref_fwd_fp8(q8, k8, v8, sq, sk, sv, scale, causal=False, block_m=128, block_
     Since e4m3(a 2^k) = 2^k e4m3(a) while both are normal numbers, every
     integer reference gives the same O up to values in the subnormal range;
     ``ref_shift`` exists to pin that.  Returns (O [..., N, d], LSE [..., N]).
+
+    With ``tie_rel`` = eps it also returns the rounding slack R [..., N, d]:
+    R_i = sum_j w_j |v_j| / l, where w_j is the gap between the E4M3
+    roundings of a_j's upper and lower error bounds (non-zero only when a tie
+    lies between them), plus one subnormal spacing 2^-9 for every
+    a_j < 2^-6.  The error bounds are a_j 2^(+-du_j) (1 +- eps), with
+    du_j = score_rel scale log2(e) max_d |q_d k_jd|: an implementation whose
+    scores are off by at most score_rel times their largest product, and
+    whose a_j carry a further relative error below eps, may round those a_j
+    the other way, or (with a reference M that leaves more a_j in the normal
+    range) round small a_j more finely; its l moves by at most a factor
+    2^Du (Du = max_j du_j + log2(1 + eps)).  Its O is then within
+    R = sum_j w_j |v_j| / l + |O| (2^Du - 1) of this one and its LSE within
+    RL = Du ln 2; with ``tie_rel`` the function returns (O, LSE, R, RL).
     """
     q8, k8, v8 = _f64(q8), _f64(k8), _f64(v8)
     N, Nk = q8.shape[-2], k8.shape[-2]
     O = np.zeros(q8.shape[:-1] + (v8.shape[-1],))
+    R = np.zeros(O.shape)
     LSE = np.full(q8.shape[:-1], NEG_INF)
+    RL = np.zeros(LSE.shape)
     for h in _heads(q8.shape):
         qd = q8[h] * _rows_of_blocks(sq[h], block_m, N)[:, None]
         kd = k8[h] * _rows_of_blocks(sk[h], block_n, Nk)[:, None]
@@ -444,4 +461,14 @@ def ref_fwd_fp8(q8, k8, v8, sq, sk, sv, scale, causal=False, block_m=128, block_
             l = a.sum()
             O[h][i] = (e4m3_round(a) @ vd) / l
             LSE[h][i] = (M + np.log2(l) - P_EXP) * np.log(2.0)
+            if tie_rel is not None:
+                du = score_rel * abs(scale) * np.log2(np.e) * np.max(np.abs(qd[i][None, :] * kd), axis=1)
+                up = np.minimum(a * np.exp2(du) * (1 + tie_rel), E4M3_MAX)
+                w = e4m3_round(up) - e4m3_round(a * np.exp2(-du) * (1 - tie_rel))
+                w = w + np.where((a > 0) & (a < 2.0 ** -6), 2.0 ** -9, 0.0)
+                Du = np.max(np.where(vis, du, 0.0)) + np.log2(1 + tie_rel)
+                R[h][i] = (w @ np.abs(vd)) / l + np.abs(O[h][i]) * (2.0 ** Du - 1)
+                RL[h][i] = Du * np.log(2.0)
+    if tie_rel is not None:
+        return O, LSE, R, RL
     return O, LSE

@@ -586,6 +586,42 @@ def test_fp8_forward_integer_reference_shift():
         np.testing.assert_allclose(L1, L0, rtol=1e-13)
 
 
+def test_fp8_forward_rounding_slack():
+    """The slack bounds how far O moves when every a_j is perturbed by a
+    relative error below eps (as an fp32 evaluation would): the perturbed
+    results, computed by rounding perturbed a_j, stay within it; with eps = 0
+    and no subnormal a_j it is zero."""
+    q8, k8, v8, sq, sk, sv = _fp8_inputs(60, 64, 76)
+    eps = 2.0 ** -6  # large, so that the perturbations below do flip roundings
+    O, _, R, _ = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125, tie_rel=eps)
+    flipped = False
+    rng = np.random.default_rng(77)
+    true_round = ar.e4m3_round
+    for _ in range(3):
+        delta = rng.uniform(-eps, eps, 60)
+
+        def jittered(x, _d=delta):
+            x = np.asarray(x, dtype=np.float64)
+            return true_round(np.minimum(x * (1 + _d[:x.shape[-1]]), 448.0)) if x.ndim == 1 and x.shape[0] == 60 \
+                else true_round(x)
+
+        ar.e4m3_round = jittered
+        try:
+            Oj, _ = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125)
+        finally:
+            ar.e4m3_round = true_round
+        assert np.all(np.abs(Oj - O) <= R + 1e-15)
+        flipped |= bool(np.any(Oj != O))
+    assert flipped
+    # uniform scores: every a_j is exactly 8, far from a tie and normal
+    O0, _, R0, RL0 = ar.ref_fwd_fp8(0 * q8, k8, v8, sq, sk, sv, 0.125, tie_rel=eps)
+    np.testing.assert_allclose(R0, np.abs(O0) * eps, rtol=1e-6)   # only l's own error remains
+    np.testing.assert_allclose(RL0, np.log1p(eps), rtol=1e-12)
+    # a score error bound widens every band, so the slack can only grow
+    _, _, R1, RL1 = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125, tie_rel=eps, score_rel=2.0 ** -9)
+    assert np.all(R1 >= R) and np.any(R1 > R) and np.all(RL1 > RL0[..., :1])
+
+
 def test_hadamard_rotation_helps_outlier_features():
     """Incoherent processing ([Triton-ch8] section 8.9.5): with a few feature
     dimensions far larger than the rest, rotating Q and K before the block
