@@ -10,6 +10,9 @@ inputs:
   * split-K decode over a paged cache holding the same K/V cache in 16-token
     blocks scattered over the pool by a random block table (reported only;
     its output must equal the dense decode's bit for bit)
+  * forward on FP8 (E4M3) storage of the headline Q, K, V (per-block
+    power-of-two scales: Q per 128 rows, K and V per 64; quantised before the
+    timed region), non-causal (reported only)
 
 `value` is the forward's TFLOP/s (4*B*H*N^2*d per call) from HIP events
 around its launch on the launch stream, averaged over the timed steps.
@@ -29,6 +32,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2516.6  # 256 CU x 4 SIMD x 1024 FLOP/clk x 2.4 GHz, dense
 PEAK_HBM_GBPS = 8000.0
+PEAK_FP8_TFLOPS = 5033.2  # dense E4M3 MFMA: twice the bf16 rate
 METRIC = "attn fwd TFLOP/s + % bf16 MFMA peak (B4 H16 N2048 d64); decode HBM GB/s"
 
 FWD = dict(B=4, H=16, N=2048, d=64, causal=False, input_scale=1.0)
@@ -36,6 +40,7 @@ FWD_LONG = dict(B=2, H=32, N=8192, d=128, causal=True, input_scale=0.5)
 DEC = dict(B=16, H=32, L=32768, d=128, S=256)
 DEC_PAGED = dict(DEC, block_size=16)
 BWD = dict(B=2, H=16, N=4096, d=64, causal=True)
+FP8_BLOCKS = (128, 64)  # rows per scale: Q, then K and V
 
 
 def fwd_flops(c):
@@ -130,13 +135,13 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--only", default="",
-                    help="comma-separated subset of fwd,decode,bwd,fwd_long,decode_paged to run "
+                    help="comma-separated subset of fwd,decode,bwd,fwd_long,decode_paged,fwd_fp8 to run "
                          "(profiling passes)")
     a = ap.parse_args()
-    parts = ["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long"]) + ["decode_paged"]
+    parts = ["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long"]) + ["decode_paged", "fwd_fp8"]
     if a.only:
         parts = [p for p in a.only.split(",") if p]
-        bad = [p for p in parts if p not in ("fwd", "decode", "bwd", "fwd_long", "decode_paged")]
+        bad = [p for p in parts if p not in ("fwd", "decode", "bwd", "fwd_long", "decode_paged", "fwd_fp8")]
         if bad:
             ap.error(f"unknown --only parts {bad}")
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -146,7 +151,8 @@ def main():
 
     import torch
 
-    from exact_attention_05_amd import attn_bwd, attn_fwd, attn_fwd_splitk_decode, attn_fwd_splitk_decode_paged
+    from exact_attention_05_amd import (attn_bwd, attn_fwd, attn_fwd_fp8, attn_fwd_splitk_decode,
+                                        attn_fwd_splitk_decode_paged, attn_quantize_fp8)
     from exact_attention_05_amd.binding import attn_bwd_workspace_bytes, attn_decode_workspace_bytes
     from exact_attention_05_amd.inputs import make_block_table, make_tensor
 
@@ -192,6 +198,15 @@ def main():
         pws = torch.empty_like(dws)
         if "decode" not in parts:
             del dk_, dv_
+    if "fwd_fp8" in parts:
+        c = FWD
+        xq, xk, xv = mk(0, ("q", "k", "v"), c["B"], c["H"], c["N"], c["d"])
+        q8, sq8 = attn_quantize_fp8(xq, FP8_BLOCKS[0])
+        k8, sk8 = attn_quantize_fp8(xk, FP8_BLOCKS[1])
+        v8, sv8 = attn_quantize_fp8(xv, FP8_BLOCKS[1])
+        del xq, xk, xv
+        o8 = torch.empty((c["B"], c["H"], c["N"], c["d"]), dtype=bf16, device=dev)
+        lse8 = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device=dev)
     if "bwd" in parts:
         c = BWD
         bq, bk, bv, bdo = mk(0, ("q", "k", "v", "do"), c["B"], c["H"], c["N"], c["d"])
@@ -234,6 +249,10 @@ def main():
             ev["fwd_long"][0].record(stream)
             attn_fwd(lq, lk, lv, causal=True, out=lo, lse=llse)
             ev["fwd_long"][1].record(stream)
+        if "fwd_fp8" in names:
+            ev["fwd_fp8"][0].record(stream)
+            attn_fwd_fp8(q8, k8, v8, sq8, sk8, sv8, FP8_BLOCKS[0], FP8_BLOCKS[1], causal=False, out=o8, lse=lse8)
+            ev["fwd_fp8"][1].record(stream)
         if "decode_paged" in names:
             ev["decode_paged"][0].record(stream)
             attn_fwd_splitk_decode_paged(dq_, pk, pv, ptab, plens, DEC["S"], out=po, lse=plse, workspace=pws)
@@ -284,7 +303,8 @@ def main():
             "workload": "attention forward bf16 [B=4,H=16,N=2048,d=64] non-causal (headline); split-K decode "
                         "bf16 q[16,32,1,128] x KV[16,32,32768,128], 256 chunks; backward bf16 [2,16,4096,64] "
                         "causal; forward bf16 [2,32,8192,128] causal (reported); the same decode over a "
-                        "paged cache of 16-token blocks (reported)",
+                        "paged cache of 16-token blocks (reported); the headline forward on FP8 E4M3 storage "
+                        "(reported)",
             "global_batch": FWD["B"],
             "seq_len": FWD["N"],
             "parallelism": "single GPU",
@@ -337,6 +357,19 @@ def main():
             "unit": "GB/s",
             "frac": round(pg / PEAK_HBM_GBPS, 4),
             "traffic": _traffic("decode_paged_d128", ["decode.hip", "common.h"]),
+        }
+    if "fwd_fp8" in ms:
+        f8 = rate("fwd_fp8", fwd_flops(FWD), 1e12)
+        out["fwd_fp8_tflops"] = round(f8, 3)
+        out["fwd_fp8_pct_fp8_peak"] = round(100.0 * f8 / PEAK_FP8_TFLOPS, 2)
+        out["fwd_fp8_us"] = round(ms["fwd_fp8"] * 1e3, 2)
+        out["roofline_fwd_fp8"] = {
+            "bound": "mfma",
+            "achieved": round(f8, 3),
+            "peak": PEAK_FP8_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(f8 / PEAK_FP8_TFLOPS, 4),
+            "traffic": _traffic("fwd_fp8_d64", ["fwd_fp8.hip", "common.h"]),
         }
     if not a.no_cpu_baseline and "fwd" in names:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)

@@ -1,5 +1,5 @@
 """MI355X-native exact attention: FA-2 style forward, split-K decode (over a
-dense or a paged cache) and recomputation backward, as hand-written HIP kernels for gfx950 behind a
+dense or a paged cache), recomputation backward and an FP8 (E4M3) forward, as hand-written HIP kernels for gfx950 behind a
 C ABI (``libattn.so``, declared in ``include/attn.h``).
 
 The Python names mirror the C entry points; the shared library is loaded on
@@ -11,6 +11,8 @@ __all__ = [
     "attn_fwd_splitk_decode",
     "attn_fwd_splitk_decode_paged",
     "attn_bwd",
+    "attn_quantize_fp8",
+    "attn_fwd_fp8",
     "attn_decode_workspace_bytes",
     "attn_bwd_workspace_bytes",
     "attn_status_string",

@@ -63,6 +63,10 @@ def _load():
     lib.attn_fwd_splitk_decode_paged.restype = ci
     lib.attn_fwd_splitk_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, ci,
                                                  ci, cf, vp]
+    lib.attn_quantize_fp8.restype = ci
+    lib.attn_quantize_fp8.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, vp]
+    lib.attn_fwd_fp8.restype = ci
+    lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp]
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci]
     lib.attn_bwd.restype = ci
@@ -207,6 +211,71 @@ def attn_fwd_splitk_decode_paged(q, k_pool, v_pool, block_table, seq_lens, num_s
         max_blocks, int(num_splits), _dtype_code(q), scale, _stream(dev))
     _check(st, "attn_fwd_splitk_decode_paged")
     return out, lse, workspace
+
+
+def _check_fp8(name, t, shape, device):
+    _require(t.is_cuda and t.device == device, f"{name} must be on {device}")
+    _require(t.element_size() == 1, f"{name} must hold one byte per element (E4M3 bit patterns)")
+    _require(tuple(t.shape) == tuple(shape), f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def attn_quantize_fp8(x, block_rows, signs=None, out=None, scales=None):
+    """Block quantisation of bf16 x [B, H, N, d] to E4M3 bytes plus one
+    power-of-two fp32 scale per block of ``block_rows`` rows, optionally after
+    the Hadamard rotation with ``signs`` (d floats of +-1).
+
+    Returns (x8 uint8 [B, H, N, d], scales fp32 [B, H, ceil(N / block_rows)]).
+    """
+    B, H, N, d = x.shape
+    dev = x.device
+    _check_bhnd("x", x, (B, H, N, d), torch.bfloat16, dev)
+    nblk = -(-N // int(block_rows))
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.uint8, device=dev)
+    else:
+        _check_fp8("out", out, (B, H, N, d), dev)
+    if scales is None:
+        scales = torch.empty((B, H, nblk), dtype=torch.float32, device=dev)
+    else:
+        _check_bhnd("scales", scales, (B, H, nblk), torch.float32, dev)
+    if signs is not None:
+        _check_bhnd("signs", signs, (d,), torch.float32, dev)
+    st = _load().attn_quantize_fp8(_ptr(x), _ptr(signs), _ptr(out), _ptr(scales), B, H, N, d, int(block_rows),
+                                   _stream(dev))
+    _check(st, "attn_quantize_fp8")
+    return out, scales
+
+
+def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, block_m, block_n, scale=None, causal=False, out=None,
+                 lse=None):
+    """Attention forward on E4M3 inputs [B, H, N, d] (uint8 bit patterns)
+    with power-of-two per-block scales (q_scale [B, H, ceil(N / block_m)],
+    k_scale and v_scale [B, H, ceil(N / block_n)]).
+
+    Returns (o bf16 [B, H, N, d], lse fp32 [B, H, N]).
+    """
+    B, H, N, d = q8.shape
+    dev = q8.device
+    for name, t in (("q8", q8), ("k8", k8), ("v8", v8)):
+        _check_fp8(name, t, (B, H, N, d), dev)
+    _check_bhnd("q_scale", q_scale, (B, H, -(-N // int(block_m))), torch.float32, dev)
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        _check_bhnd(name, t, (B, H, -(-N // int(block_n))), torch.float32, dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    else:
+        _check_bhnd("out", out, (B, H, N, d), torch.bfloat16, dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    else:
+        _check_bhnd("lse", lse, (B, H, N), torch.float32, dev)
+    st = _load().attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v8), _ptr(q_scale), _ptr(k_scale), _ptr(v_scale), _ptr(out),
+                              _ptr(lse), B, H, N, d, int(block_m), int(block_n), scale, int(bool(causal)),
+                              _stream(dev))
+    _check(st, "attn_fwd_fp8")
+    return out, lse
 
 
 def split_decode_workspace(workspace, B, H, d, num_splits):

@@ -113,6 +113,36 @@ attn_status attn_fwd_splitk_decode_paged(const void* q, const void* k_pool, cons
   return from_hip(attn::launch_decode_paged_bf16(a, p, static_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_quantize_fp8(const void* x, const float* signs, void* x8, float* scales, int B, int H, int N, int d,
+                              int block_rows, void* stream) {
+  if (B < 1 || H < 1 || N < 1 || N > (1 << 24) || d < 1 || block_rows < 1) return ATTN_ERR_INVALID_ARG;
+  const int64_t nblk = ((int64_t)N + block_rows - 1) / block_rows;
+  if ((int64_t)B * H * nblk > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  if (!tensor_ok(x) || !tensor_ok(x8)) return ATTN_ERR_INVALID_ARG;
+  if (scales == nullptr || !aligned(scales, 4)) return ATTN_ERR_INVALID_ARG;
+  if (signs != nullptr && !aligned(signs, 4)) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  if (signs != nullptr && d != 64) return ATTN_ERR_UNSUPPORTED;
+  attn::QuantArgs a{x, signs, x8, scales, B, H, N, d, block_rows};
+  return from_hip(attn::launch_quantize_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale, const float* k_scale,
+                         const float* v_scale, void* o, float* lse, int B, int H, int N, int d, int block_m,
+                         int block_n, float scale, int causal, void* stream) {
+  attn_status st = check_common(B, H, N, d, ATTN_BF16, scale);
+  if (st != ATTN_OK) return st;
+  if (block_m < 32 || block_m % 32 != 0 || block_n < 64 || block_n % 64 != 0) return ATTN_ERR_INVALID_ARG;
+  if (!tensor_ok(q8) || !tensor_ok(k8) || !tensor_ok(v8) || !tensor_ok(o)) return ATTN_ERR_INVALID_ARG;
+  for (const float* p : {q_scale, k_scale, v_scale})
+    if (p == nullptr || !aligned(p, 4)) return ATTN_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
+  if (d != 64) return ATTN_ERR_UNSUPPORTED;
+  attn::Fp8FwdArgs a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, block_m, block_n, scale,
+                     causal != 0};
+  return from_hip(attn::launch_fwd_fp8(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t attn_bwd_workspace_bytes(int B, int H, int N) {
   if (B < 1 || H < 1 || N < 1) return 0;
   return (size_t)B * (size_t)H * (size_t)N * 24;

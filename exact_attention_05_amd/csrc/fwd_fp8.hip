@@ -1,0 +1,480 @@
+// FP8 (E4M3) attention forward and block quantisation for gfx950
+// ("8. FlashAttention 实战", triton-tutorial.pages.dev, section 8.9).
+//
+// Storage: Q, K, V in E4M3 with one scale per block of rows (section 8.9.4).
+// The scales are powers of two, so the matrix unit applies them:
+// v_mfma_scale_f32_32x32x64_f8f6f4 takes an E8M0 exponent per row of A and
+// per column of B (for each 32-wide half of the reduction), which is the
+// exponent field of the fp32 scale.  Dequantisation therefore costs nothing.
+//
+// Forward (d = 64), the scheme of the bf16 d = 64 kernel in fwd.hip: 16
+// wavefronts of 32 query rows, four per SIMD in two groups one phase apart,
+// 64-key K/V tiles copied HBM -> LDS ahead of use.  Per tile and wavefront:
+//   S^T = K Q^T   two MFMAs (keys 0-31, 32-63), reduction over d = 64 in one
+//                 instruction; scale_a = the K block's exponent, scale_b = the
+//                 query row's Q block exponent;
+//   P~ = 2^(s log2(e) scale - M + 3), M an integer reference per row, summed
+//                 unrounded into l and rounded to E4M3 for the next product
+//                 (section 8.9.3: softmax statistics in high precision, P
+//                 requantised to FP8);
+//   O^T += V^T P~^T  two MFMAs (d rows 0-31, 32-63), reduction over the 64
+//                 keys; scale_a = the V block's exponent.
+// P~ goes from the score accumulator straight into the B operand (a lane
+// holds 32 keys of its query); the V^T operand is read with transposing
+// 8-bit LDS reads whose source rows follow the same key order.
+//
+// Reference M: the ceiling of the row max of the first tile (key 0 is visible
+// to every row).  P~ <= 2^3 while no score exceeds M; a lane checks that the
+// sum of its 32 P~ stays <= 448 (so no single value can exceed the largest
+// E4M3 number), and otherwise the wavefront moves M to the ceiling of the
+// running max, rescales U and l by the exact power of two 2^(M_old - M_new)
+// and redoes the tile.  Because M is an integer, E4M3 rounding of P~ does not
+// depend on which reference is used (up to values in the subnormal range).
+#include "common.h"
+#include "launch.h"
+
+namespace attn {
+namespace {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kFp8Bc = 64;        // keys per tile
+constexpr int kFp8Row = 64;       // bytes per row (d = 64, one byte each)
+constexpr int kFp8Tile = 64 * 64; // bytes per K or V tile
+constexpr float kP8Max = 448.f;   // largest finite E4M3 value
+constexpr float kPExp = 3.f;      // P~ = 2^(u - M + kPExp)
+constexpr int kE8One = 127;       // E8M0 encoding of 1.0
+
+// E8M0 exponent of a power-of-two fp32 scale: its biased exponent field.
+__device__ __forceinline__ int e8m0_of(float s) { return (__float_as_uint(s) >> 23) & 0xFF; }
+
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+}
+
+// Transposing LDS read of 8-bit values (ds_read_b64_tr_b8).  Within every
+// group of 16 lanes each lane names 8 bytes; lane i of the group receives, as
+// its byte q, byte (i % 8) of the 8 bytes named by lane 2q + i / 8.
+__device__ __forceinline__ i32x2 lds_read_tr8(const void* lds_addr) {
+  return __builtin_amdgcn_ds_read_tr8_b64_v2i32((__attribute__((address_space(3))) i32x2*)lds_addr);
+}
+
+// FP8 tile: 64 rows x 64 bytes, row k at byte 64k, its 16-byte chunk c stored
+// at chunk c ^ ((k >> 2) & 3).  Both operand reads then touch every LDS bank
+// once per pass: 16 consecutive rows x one chunk (ds_read_b128), and 8 rows
+// {k0..k0+3, k0+8..k0+11} x 4 chunk-halves (ds_read_b64_tr_b8, 32 lanes).
+__device__ __forceinline__ int fp8_off(int k, int c) { return 64 * k + 16 * (c ^ ((k >> 2) & 3)); }
+
+// Key of byte J of a lane in half h of the P~ operand: the score
+// accumulator's row order (block J / 16, accumulator index J % 16).
+__device__ __forceinline__ constexpr int pkey(int h, int J) { return 32 * (J >> 4) + acc_row(J & 15, h); }
+
+// ---------------------------------------------------------------------------
+// Forward kernel, d = 64.  Work ids, ring of five tiles, phase structure and
+// barriers as fwd_pp4_kernel; waves 0-3 copy the K tile and 4-7 the V tile.
+// ---------------------------------------------------------------------------
+template <bool CAUSAL>
+__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void fwd_fp8_kernel(
+    const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
+    const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
+    __bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg, int block_m,
+    int block_n, float scale_log2) {
+  constexpr int D = 64;
+  constexpr int NW = 16;
+  constexpr int BR = NW * 32;
+  constexpr int TB = 2 * kFp8Tile;  // K | V
+  __shared__ __attribute__((aligned(1024))) unsigned char sb0[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb1[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb2[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb3[TB];
+  __shared__ __attribute__((aligned(1024))) unsigned char sb4[TB];
+
+  const int lid = xcd_remap(blockIdx.x, total_wg);
+  const int bh = lid / n_qtiles;
+  int qtile = lid % n_qtiles;
+  if (CAUSAL) qtile = n_qtiles - 1 - qtile;  // longest rows first
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool lead = wave < NW / 2;
+  const int g = lane >> 5, l32 = lane & 31;
+  const int64_t base = (int64_t)bh * N * D;
+  const int q0 = qtile * BR;
+  const int qw0 = q0 + wave * 32;
+  const int qr = qw0 + l32;
+  const int kend = CAUSAL ? min(N, q0 + BR) : N;
+  const int ntiles = (kend + kFp8Bc - 1) / kFp8Bc;
+  const int nkb = (N + block_n - 1) / block_n;
+  const float* ksh = KS + (int64_t)bh * nkb;
+  const float* vsh = VS + (int64_t)bh * nkb;
+
+  // copy geometry: waves 0-3 fill the K tile, 4-7 the V tile, 1 KB each;
+  // lane l fills physical chunk l % 4 of row 16 (wave % 4) + l / 4.
+  const bool copier = wave < 8;
+  const uint8_t* csrc = (wave < 4 ? K : V) + base;  // wave-uniform
+  const int crow = 16 * (wave & 3) + (lane >> 2);
+  const int ccol = 16 * ((lane & 3) ^ ((crow >> 2) & 3));
+  const int cdst = (wave < 4 ? 0 : kFp8Tile) + 1024 * (wave & 3);
+  auto issue_tile = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
+    if (copier) {
+      // rows past N read row N-1 (masked later); a head spans < 2^31 bytes
+      const uint32_t off = (uint32_t)(min(j * kFp8Bc + crow, N - 1) * kFp8Row + ccol);
+      global_to_lds16(csrc + off, buf + cdst);
+    }
+  };
+
+  issue_tile(0, sb0);
+  if (ntiles > 1) issue_tile(1, sb1);
+  if (ntiles > 2) issue_tile(2, sb2);
+
+  // Q row of this lane: bytes 32g .. 32g+31 (the B operand's reduction half g)
+  i32x8 qB = {};
+  if (qr < N) {
+    const u32x4* qp = reinterpret_cast<const u32x4*>(Q + base + (int64_t)qr * kFp8Row + 32 * g);
+    const u32x4 a = qp[0], b = qp[1];
+    qB = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+  }
+  // block_m is a multiple of 32, so the wavefront's rows share one Q scale
+  const int qexp =
+      __builtin_amdgcn_readfirstlane(e8m0_of(QS[(int64_t)bh * ((N + block_m - 1) / block_m) + min(qw0, N - 1) / block_m]));
+
+  // Per-lane LDS offsets.  K rows (S operand): chunks 2g and 2g+1 of row
+  // l32; rows 32 further (the second key half) share the swizzle phase, +2048.
+  const int koff0 = fp8_off(l32, 2 * g), koff1 = fp8_off(l32, 2 * g + 1);
+  // Transposed V (O operand): the source lane of read t names key
+  // pkey(G / 2, 8t + q) = 16t + kl and dims 32mt + 16(G % 2) + 8p; the key's
+  // swizzle phase does not depend on t (+1024 per read), and d block mt = 1
+  // flips bit 1 of the chunk (XOR 32).
+  int voff0;
+  {
+    const int G = lane >> 4, s = lane & 15, qq = s >> 1, pp = s & 1;
+    voff0 = fp8_off(pkey(G >> 1, qq), G & 1) + 8 * pp;
+  }
+
+  f32x16 oacc[2] = {f32x16{}, f32x16{}};
+  float M = kNegInf, lsum = 0.f, rs = 0.f;
+  f32x16 sacc[2];
+  i32x8 pb;  // P~ of the current tile as E4M3, the B operand of O^T += V^T P~^T
+  int kexp = e8m0_of(ksh[0]);
+  int vexp = kexp, vexp_prev = kexp;
+
+  // MFMA operands, all read from LDS at the top of the matrix phase so that
+  // their latencies overlap (V^T of the previous tile, K of this one).
+  i32x8 va[2], ka[2];
+  auto read_k = [&](const unsigned char* kt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const u32x4 a = *reinterpret_cast<const u32x4*>(kt + koff0 + 2048 * hb);
+      const u32x4 b = *reinterpret_cast<const u32x4*>(kt + koff1 + 2048 * hb);
+      ka[hb] = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+    }
+  };
+  auto read_v = [&](const unsigned char* vt) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int vo = mt ? (voff0 ^ 32) : voff0;
+      i32x2 r[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) r[t] = lds_read_tr8(vt + vo + 1024 * t);
+      va[mt] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
+    }
+  };
+  auto scores = [&](int ke) __attribute__((always_inline)) {
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) sacc[hb] = mfma_fp8(ka[hb], qB, f32x16{}, ke, qexp);
+  };
+  // M: O^T += V^T P~^T of the previous tile, then S^T of this one, from the
+  // operands read at the end of the previous vector phase.
+  // `copy` runs after the operand reads: a tile copy issued before them makes
+  // the compiler wait for it (it cannot always tell the buffers apart).
+  auto mph = [&](const unsigned char* kt, const unsigned char* vt, const bool do_pv, const bool do_s,
+                 auto&& copy) __attribute__((always_inline)) {
+    if (do_pv) read_v(vt + kFp8Tile);
+    if (do_s) read_k(kt);
+    copy();
+    __builtin_amdgcn_s_setprio(1);
+    if (do_pv) {
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) oacc[mt] = mfma_fp8(va[mt], pb, oacc[mt], vexp_prev, kE8One);
+    }
+    if (do_s) scores(kexp);
+    // keep the products in this phase (the barrier after it orders memory only)
+    if (do_pv) asm volatile("" : "+v"(oacc[0]), "+v"(oacc[1]));
+    if (do_s) asm volatile("" : "+v"(sacc[0]), "+v"(sacc[1]));
+    __builtin_amdgcn_s_setprio(0);
+  };
+
+  auto mask_tile = [&](int j) __attribute__((always_inline)) {
+    const int kb = j * kFp8Bc;
+    if ((kb + kFp8Bc > N) || (CAUSAL && kb + kFp8Bc - 1 > qw0)) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kb + 32 * hb + acc_row(i, g);
+          const bool vis = key < N && (!CAUSAL || key <= qr);
+          if (!vis) sacc[hb][i] = kNegInf;
+        }
+    }
+  };
+  auto row_max_ceil = [&]() __attribute__((always_inline)) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[1][i]));
+    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
+    return ceilf(mx * scale_log2);
+  };
+  // P~ = 2^(s c - M + 3) in E4M3 (byte J of the lane = key pkey(g, J)); rs = fp32 sum
+  auto expo = [&]() __attribute__((always_inline)) {
+    const float off = kPExp - M;
+    float r4[4];
+#pragma unroll
+    for (int w = 0; w < 8; ++w) {
+      float x[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = fast_exp2(fmaf(sacc[w >> 2][4 * (w & 3) + e], scale_log2, off));
+      if ((w & 1) == 0) r4[w >> 1] = (x[0] + x[1]) + (x[2] + x[3]);
+      else r4[w >> 1] += (x[0] + x[1]) + (x[2] + x[3]);
+      const int pw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+      pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], pw, true);
+    }
+    rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+  };
+  // V(j): tile j is at cur (its K is read again only by the rare rescue).
+  auto vph = [&](int j, const unsigned char* cur) __attribute__((always_inline)) {
+    mask_tile(j);
+    if (j == 0) M = row_max_ceil();
+    expo();
+    if (__builtin_expect(__ballot(!(rs <= kP8Max)) != 0, 0)) {
+      // rare: a P~ could exceed the E4M3 range; move the reference up and redo the tile
+      __builtin_amdgcn_sched_barrier(0);
+      read_k(cur);
+      scores(kexp);
+      mask_tile(j);
+      const float mn = fmaxf(M, row_max_ceil());
+      const float alpha = fast_exp2(M - mn);  // an exact power of two
+      M = mn;
+      lsum *= alpha;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) oacc[mt] *= alpha;
+      expo();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    lsum += rs;
+    asm volatile("" : "+v"(pb));
+  };
+  // scale exponents of tile j+1, read while tile j is processed
+  auto next_scales = [&](int j) __attribute__((always_inline)) {
+    vexp_prev = vexp;
+    if (j + 1 < ntiles) {
+      const int kb = ((j + 1) * kFp8Bc) / block_n;
+      kexp = e8m0_of(ksh[kb]);
+      vexp = e8m0_of(vsh[kb]);
+    }
+  };
+  vexp = e8m0_of(vsh[0]);
+
+  if (ntiles > 2) wait_vm_at_most<2>(); else if (ntiles > 1) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
+  lds_barrier();
+  if (!lead) lds_barrier();
+  mph(sb0, sb0, false, true, [&]() __attribute__((always_inline)) { if (ntiles > 3) issue_tile(3, sb3); });
+  if (ntiles > 3) wait_vm_at_most<2>(); else if (ntiles > 2) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
+  lds_barrier();
+  vph(0, sb0);
+  next_scales(0);
+  // Tile j at cur, j-1 at prev; tile j+3 goes to far (the slot of j-2).
+  auto step = [&](int j, const unsigned char* cur, const unsigned char* prev, unsigned char* far)
+      __attribute__((always_inline)) {
+    lds_barrier();
+    mph(cur, prev, true, true, [&]() __attribute__((always_inline)) { if (j + 3 < ntiles) issue_tile(j + 3, far); });
+    if (j + 3 < ntiles) wait_vm_at_most<2>(); else if (j + 2 < ntiles) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
+    lds_barrier();
+    vph(j, cur);
+    next_scales(j);
+  };
+  for (int j = 1; j < ntiles; j += 5) {
+    step(j, sb1, sb0, sb4);
+    if (j + 1 < ntiles) step(j + 1, sb2, sb1, sb0);
+    if (j + 2 < ntiles) step(j + 2, sb3, sb2, sb1);
+    if (j + 3 < ntiles) step(j + 3, sb4, sb3, sb2);
+    if (j + 4 < ntiles) step(j + 4, sb0, sb4, sb3);
+  }
+  lds_barrier();
+  {
+    const int t = (ntiles - 1) % 5;
+    const unsigned char* last = t == 0 ? sb0 : t == 1 ? sb1 : t == 2 ? sb2 : t == 3 ? sb3 : sb4;
+    mph(last, last, true, false, []() {});
+  }
+  if (lead) lds_barrier();
+
+  const float lt = lsum + shfl_xor_f32(lsum, 32);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  if (qr < N) {
+    __bf16* Oh = O + base;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int d0 = 32 * mt + 8 * c + 4 * g;
+        u32x2 w = {pack_bf16x2(oacc[mt][4 * c] * inv, oacc[mt][4 * c + 1] * inv),
+                   pack_bf16x2(oacc[mt][4 * c + 2] * inv, oacc[mt][4 * c + 3] * inv)};
+        *reinterpret_cast<u32x2*>(Oh + (int64_t)qr * D + d0) = w;
+      }
+    if (g == 0 && LSE != nullptr)
+      LSE[(int64_t)bh * N + qr] = lt > 0.f ? (M + fast_log2(lt) - kPExp) * kLn2 : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Block quantisation: one workgroup per block of rows of one (b, h).  Each
+// thread holds 8 consecutive values of a row (D / 8 threads per row).  With
+// signs, each row is first rotated, y = (x o signs) H / sqrt(D) (fast
+// Walsh-Hadamard transform: three butterfly stages inside the thread, the
+// rest across the row's lanes).  Pass 1 takes max|y| over the block; the
+// scale is 2^k, the smallest power of two with 448 2^k >= max|y| (k >= -126,
+// 1 for a zero block); pass 2 writes e4m3(y 2^-k), rounded to nearest even.
+// ---------------------------------------------------------------------------
+template <int D, bool ROT>
+__global__ __launch_bounds__(256) void quant_fp8_kernel(const __bf16* __restrict__ X, const float* __restrict__ signs,
+                                                        uint8_t* __restrict__ X8, float* __restrict__ scales,
+                                                        int N, int block_rows, int nblk) {
+  constexpr int TPR = D / 8;        // threads per row
+  constexpr int RPP = 256 / TPR;    // rows per pass
+  __shared__ float red[4];
+  const int bh = blockIdx.x / nblk;
+  const int b = blockIdx.x % nblk;
+  const int r0 = b * block_rows;
+  const int r1 = min(r0 + block_rows, N);
+  const int tid = threadIdx.x;
+  const int u = tid % TPR;          // dims 8u .. 8u+7
+  const __bf16* Xh = X + (int64_t)bh * N * D;
+
+  float sg[8];
+  if constexpr (ROT) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sg[e] = signs[8 * u + e];
+  }
+  auto load_row = [&](int r, float (&y)[8]) __attribute__((always_inline)) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(Xh + (int64_t)r * D + 8 * u);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      y[2 * e] = bf16lo_to_f32(w[e]);
+      y[2 * e + 1] = bf16hi_to_f32(w[e]);
+    }
+    if constexpr (ROT) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= sg[e];
+#pragma unroll
+      for (int hb = 1; hb < 8; hb <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if ((e & hb) == 0) {
+            const float a = y[e], c = y[e + hb];
+            y[e] = a + c;
+            y[e + hb] = a - c;
+          }
+#pragma unroll
+      for (int lb = 1; lb < TPR; lb <<= 1) {
+        const bool hi = (u & lb) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float o = shfl_xor_f32(y[e], lb);
+          y[e] = hi ? o - y[e] : y[e] + o;
+        }
+      }
+      static_assert(D == 64, "rotation normalisation is exact only for d = 64");
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] *= 0.125f;  // 1 / sqrt(64)
+    }
+  };
+
+  // Every thread runs the same number of passes (the rotation's shuffles need
+  // all lanes of a row); rows past the block read row r0 and are discarded.
+  const int npass = (r1 - r0 + RPP - 1) / RPP;
+
+  // pass 1: max |y| over the block
+  float amax = 0.f;
+  for (int p = 0; p < npass; ++p) {
+    const int r = r0 + p * RPP + tid / TPR;
+    float y[8];
+    const bool ok = r < r1;
+    load_row(ok ? r : r0, y);
+    if (ok) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[e]));
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) amax = fmaxf(amax, shfl_xor_f32(amax, m));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+
+  // k: smallest integer with 448 2^k >= amax (448 = 1.75 2^8), clamped to >= -126
+  int k = 0;
+  if (amax > 0.f) {
+    const uint32_t bits = __float_as_uint(amax);
+    const int e = (int)((bits >> 23) & 0xFF) - 127;
+    k = ((bits >> 23) & 0xFF) == 0 ? -126 : ((bits & 0x7FFFFF) <= 0x600000u ? e - 8 : e - 7);
+    k = max(k, -126);
+  }
+  if (tid == 0) scales[(int64_t)bh * nblk + b] = ldexpf(1.f, k);
+
+  // pass 2: codes
+  uint8_t* X8h = X8 + (int64_t)bh * N * D;
+  for (int p = 0; p < npass; ++p) {
+    const int r = r0 + p * RPP + tid / TPR;
+    float y[8];
+    const bool ok = r < r1;
+    load_row(ok ? r : r0, y);
+    if (ok) {
+      uint32_t w[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float z[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) z[e] = fminf(fmaxf(ldexpf(y[4 * h + e], -k), -kP8Max), kP8Max);
+        int pw = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], 0, false);
+        w[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], pw, true);
+      }
+      *reinterpret_cast<u32x2*>(X8h + (int64_t)r * D + 8 * u) = u32x2{w[0], w[1]};
+    }
+  }
+}
+
+template <bool CAUSAL>
+hipError_t run_fp8(const Fp8FwdArgs& a, hipStream_t s) {
+  constexpr int BR = 16 * 32;
+  const int n_qtiles = (a.N + BR - 1) / BR;
+  const int total = n_qtiles * a.B * a.H;
+  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL>), dim3(total), dim3(1024), 0, s, static_cast<const uint8_t*>(a.q),
+                     static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), a.q_scale, a.k_scale,
+                     a.v_scale, static_cast<__bf16*>(a.o), a.lse, a.N, n_qtiles, total, a.block_m, a.block_n,
+                     a.scale * kLog2e);
+  return hipGetLastError();
+}
+
+template <int D, bool ROT>
+hipError_t run_quant(const QuantArgs& a, hipStream_t s) {
+  const int nblk = (a.N + a.block_rows - 1) / a.block_rows;
+  const int64_t grid = (int64_t)a.B * a.H * nblk;
+  hipLaunchKernelGGL((quant_fp8_kernel<D, ROT>), dim3((unsigned)grid), dim3(256), 0, s,
+                     static_cast<const __bf16*>(a.x), a.signs, static_cast<uint8_t*>(a.x8), a.scales, a.N,
+                     a.block_rows, nblk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t s) {
+  return a.causal ? run_fp8<true>(a, s) : run_fp8<false>(a, s);
+}
+
+hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t s) {
+  if (a.signs != nullptr) return run_quant<64, true>(a, s);
+  return a.d == 64 ? run_quant<64, false>(a, s) : run_quant<128, false>(a, s);
+}
+
+}  // namespace attn

@@ -44,6 +44,37 @@ struct PagedArgs {
 
 hipError_t launch_decode_paged_bf16(const DecodeArgs& a, const PagedArgs& p, hipStream_t s);
 
+// FP8 forward: q, k, v are E4M3 [B, H, N, d]; scales are powers of two per
+// block of rows (block_m for Q, block_n for K and V); o is bf16.
+struct Fp8FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* q_scale;
+  const float* k_scale;
+  const float* v_scale;
+  void* o;
+  float* lse;  // may be null
+  int B, H, N, d, block_m, block_n;
+  float scale;
+  int causal;
+};
+
+hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t s);
+
+// Block quantisation of a bf16 [B, H, N, d] tensor to E4M3 plus one
+// power-of-two scale per block of rows; signs (d values of +-1) turn on the
+// Hadamard rotation.
+struct QuantArgs {
+  const void* x;
+  const float* signs;  // may be null
+  void* x8;
+  float* scales;
+  int B, H, N, d, block_rows;
+};
+
+hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t s);
+
 struct BwdArgs {
   const void* q;
   const void* k;

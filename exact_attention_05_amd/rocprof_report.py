@@ -34,6 +34,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 
 PEAK_BF16_TFLOPS = 2516.6
+PEAK_FP8_TFLOPS = 2 * PEAK_BF16_TFLOPS  # dense E4M3 MFMA
 PEAK_HBM_GBPS = 8000.0
 COPY_KERNEL = r"copyBuffer"
 
@@ -106,7 +107,7 @@ def cmd_stats(a):
     rows = kernel_stats(a.dir)
     work = {}
     for spec in a.work or []:
-        # REGEX=AMOUNT:UNIT with UNIT in {flop, byte}
+        # REGEX=AMOUNT:UNIT with UNIT in {flop, flop8, byte} (flop8: FP8 products)
         rx, rest = spec.rsplit("=", 1)
         amt, unit = rest.split(":")
         work[rx] = (float(amt), unit)
@@ -117,9 +118,10 @@ def cmd_stats(a):
         ach = ""
         for rx, (amt, unit) in work.items():
             if re.search(rx, name):
-                if unit == "flop":
+                if unit in ("flop", "flop8"):
                     t = amt / (avg * 1e-9) / 1e12
-                    ach = f"{t:.1f} TFLOP/s = {100 * t / PEAK_BF16_TFLOPS:.1f}% of bf16 MFMA"
+                    peak, kind = (PEAK_FP8_TFLOPS, "FP8") if unit == "flop8" else (PEAK_BF16_TFLOPS, "bf16")
+                    ach = f"{t:.1f} TFLOP/s = {100 * t / peak:.1f}% of {kind} MFMA"
                 else:
                     g = amt / (avg * 1e-9) / 1e9
                     ach = f"{g:.1f} GB/s = {100 * g / PEAK_HBM_GBPS:.1f}% of HBM"
@@ -209,7 +211,7 @@ def main(argv=None):
     s.add_argument("--title", required=True)
     s.add_argument("--cmd", required=True)
     s.add_argument("--out")
-    s.add_argument("--work", action="append", help="REGEX=AMOUNT:flop|byte per launch")
+    s.add_argument("--work", action="append", help="REGEX=AMOUNT:flop|flop8|byte per launch")
     s.set_defaults(fn=cmd_stats)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)

@@ -1,7 +1,7 @@
 /*
  * attn.h -- C ABI of libattn.so: exact attention on AMD MI355X (gfx950).
  *
- * Four entry points, each an FA-2 style tiled computation that never writes
+ * The attention entry points are FA-2 style tiled computation that never writes
  * the N x N score or probability matrix to device memory:
  *
  *   attn_fwd                O = softmax(scale * Q K^T) V and the per-row
@@ -13,6 +13,9 @@
  *                           the same decode over a paged cache addressed
  *                           through a per-sequence block table.
  *   attn_bwd                dQ, dK, dV by recomputing P from the saved LSE.
+ *   attn_quantize_fp8, attn_fwd_fp8
+ *                           FP8 (E4M3) storage with per-block scales, and
+ *                           the forward on it.
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers, owned by the caller.  The
@@ -167,6 +170,68 @@ attn_status attn_fwd_splitk_decode_paged(const void* q, const void* k_pool, cons
                                          int H, int d, int num_blocks, int block_size,
                                          int max_blocks_per_seq, int num_splits, attn_dtype dtype,
                                          float scale, void* stream);
+
+/*
+ * attn_quantize_fp8 -- block quantisation of a bf16 tensor to FP8 (E4M3),
+ * the storage format of attn_fwd_fp8 ("8. FlashAttention 实战",
+ * triton-tutorial.pages.dev, sections 8.9.3-8.9.4, and 8.9.5 for the
+ * rotation).
+ *
+ * Rows of each (b, h) are grouped into blocks of `block_rows` (the last one
+ * may be shorter).  Optionally every row is first rotated,
+ * y = (x o signs) H / sqrt(d) with H the Sylvester Hadamard matrix (an
+ * orthogonal map: rotating Q and K with the same signs leaves Q K^T
+ * unchanged).  Each block gets one scale, the smallest power of two 2^k with
+ * 448 * 2^k >= max|y| (k >= -126; 1 for an all-zero block), and its values
+ * become e4m3(y / 2^k), rounded to nearest even.  The page's scale is
+ * max|y| / 448; a power of two keeps y / scale exact and lets the matrix
+ * unit apply the scale in attn_fwd_fp8.
+ *
+ *   x          : [B, H, N, d] bf16
+ *   signs      : d floats, each +1 or -1, DEVICE memory; NULL = no rotation
+ *   x8         : [B, H, N, d] bytes (E4M3 bit patterns, written)
+ *   scales     : [B, H, ceil(N / block_rows)] fp32 (written)
+ *   block_rows : >= 1
+ *
+ * Supported: d in {64, 128}; the rotation for d == 64 only.
+ * Errors: ATTN_ERR_INVALID_ARG for NULL or misaligned pointers (x, x8 16
+ * bytes; scales, signs 4 bytes) or sizes out of range; ATTN_ERR_UNSUPPORTED
+ * for another d or a rotation with d != 64.
+ */
+attn_status attn_quantize_fp8(const void* x, const float* signs, void* x8, float* scales, int B, int H,
+                              int N, int d, int block_rows, void* stream);
+
+/*
+ * attn_fwd_fp8 -- attention forward on FP8 (E4M3) inputs with per-block
+ * scales ("8. FlashAttention 实战", section 8.9.3): the two products run on
+ * FP8 with fp32 accumulation, the softmax statistics in fp32, and the
+ * probabilities are requantised to FP8 before the second product.
+ *
+ * With the dequantised inputs q = q8 * sq, k = k8 * sk, v = v8 * sv (each
+ * row's value times its block's scale), per query row i:
+ *     u_j = scale * q_i . k_j * log2(e)             (masked if causal)
+ *     a_j = 2^(u_j - M_i + 3)   with M_i an integer reference (the kernel
+ *           takes the ceiling of a running row max)
+ *     l_i = sum_j a_j                                (not rounded)
+ *     O_i = sum_j e4m3(a_j) v_j / l_i,   LSE_i = (M_i + log2 l_i - 3) ln 2
+ * E4M3 rounding commutes with scaling by powers of two, so the result does
+ * not depend on the choice of M_i except for a_j below 2^-6 (the subnormal
+ * range).  This replaces the page's data-dependent per-block scale of P with
+ * a fixed one.
+ *
+ *   q8, k8, v8 : [B, H, N, d] E4M3 bytes (as written by attn_quantize_fp8)
+ *   q_scale    : [B, H, ceil(N / block_m)] fp32;  k_scale, v_scale:
+ *                [B, H, ceil(N / block_n)] fp32.  Every scale must be a power
+ *                of two in [2^-126, 2^127]: only its exponent field is read.
+ *   o          : [B, H, N, d] bf16 (written);  lse: [B, H, N] fp32 or NULL
+ *   block_m    : a multiple of 32;  block_n: a multiple of 64
+ *
+ * Supported: d == 64.
+ * Errors as attn_fwd.
+ */
+attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
+                         const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H,
+                         int N, int d, int block_m, int block_n, float scale, int causal, void* stream);
 
 /*
  * Workspace size in bytes that attn_bwd needs: 24 bytes per query row

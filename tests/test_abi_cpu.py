@@ -30,6 +30,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("attn_fwd", "attn_fwd_splitk_decode", "attn_fwd_splitk_decode_paged", "attn_bwd",
+              "attn_quantize_fp8", "attn_fwd_fp8",
               "attn_decode_workspace_bytes",
               "attn_bwd_workspace_bytes", "attn_status_string", "attn_abi_version"):
         assert n in names
@@ -151,6 +152,51 @@ def test_paged_decode_validation():
     assert call(d=64, dt=F32) == UNSUPPORTED
     assert call(ws=NULL) == WORKSPACE
     assert call(wsb=ws_need - 1) == WORKSPACE
+
+
+def test_quantize_fp8_validation():
+    lib = _lib()
+    f = lib.attn_quantize_fp8
+    S4 = ctypes.c_void_p(0x10004)
+    base = dict(x=P, signs=NULL, x8=P, sc=S4, B=1, H=2, N=100, d=64, br=32)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["x"], a["signs"], a["x8"], a["sc"], a["B"], a["H"], a["N"], a["d"], a["br"], None)
+
+    assert call(x=NULL) == INVALID
+    assert call(x8=MIS) == INVALID
+    assert call(sc=NULL) == INVALID
+    assert call(sc=ctypes.c_void_p(0x10002)) == INVALID
+    assert call(signs=ctypes.c_void_p(0x10001)) == INVALID
+    assert call(N=0) == INVALID
+    assert call(br=0) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(d=128, signs=S4) == UNSUPPORTED
+
+
+def test_fwd_fp8_validation():
+    lib = _lib()
+    f = lib.attn_fwd_fp8
+    S4 = ctypes.c_void_p(0x10004)
+    base = dict(q=P, k=P, v=P, qs=S4, ks=S4, vs=S4, o=P, lse=NULL, B=1, H=2, N=100, d=64, bm=32, bn=64,
+                sc=0.125, causal=0)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["q"], a["k"], a["v"], a["qs"], a["ks"], a["vs"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                 a["d"], a["bm"], a["bn"], a["sc"], a["causal"], None)
+
+    assert call(q=NULL) == INVALID
+    assert call(v=MIS) == INVALID
+    assert call(ks=NULL) == INVALID
+    assert call(vs=ctypes.c_void_p(0x10002)) == INVALID
+    assert call(lse=ctypes.c_void_p(0x10002)) == INVALID
+    for bm, bn in ((0, 64), (16, 64), (48, 64), (32, 32), (32, 96), (32, 0)):
+        assert call(bm=bm, bn=bn) == INVALID, (bm, bn)
+    assert call(N=0) == INVALID
+    assert call(sc=0.0) == INVALID
+    assert call(d=128) == UNSUPPORTED
 
 
 def test_bwd_validation():
