@@ -88,21 +88,41 @@ def _traffic(kernel_key, src_names, launches_bytes_unit=None):
     return ent.get("bytes_per_launch")
 
 
+def _host_info():
+    """CPU model and BLAS threading of this host (recorded with the baselines)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+
+        pools = threadpool_info()
+        cores = max((i.get("num_threads", 1) for i in pools), default=1)
+        blas = ", ".join(sorted({f"{i.get('internal_api')} ({i.get('num_threads')} threads)" for i in pools}))
+    except Exception:  # pragma: no cover
+        cores, blas = os.cpu_count() or 1, "unknown"
+    try:
+        visible = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        visible = os.cpu_count() or 1
+    return model, int(cores), blas, visible
+
+
 def cpu_baseline(budget_s=12.0):
     """The fp64 oracle on a bounded sample of the forward workload (whole
     heads of [4, 16, 2048, 64]), on this host's cores; TFLOP/s over the sample."""
-    import numpy as np
     import torch
 
     from exact_attention_05_amd.inputs import make_head, widen
     from oracle import ref_fwd
 
-    try:
-        from threadpoolctl import threadpool_info
-
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
-    except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
+    model, cores, blas, visible = _host_info()
     c = FWD
     scale = 1.0 / math.sqrt(c["d"])
     heads = 0
@@ -115,14 +135,56 @@ def cpu_baseline(budget_s=12.0):
         t_total += time.perf_counter() - t0
         heads += 1
     flops = 4.0 * heads * c["N"] ** 2 * c["d"]
-    del np
     return {
         "value": round(flops / t_total / 1e12, 6),
         "unit": "TFLOP/s",
-        "cores": int(cores),
+        "cores": cores,
         "kind": "oracle",
         "sample": f"{heads} of {c['B'] * c['H']} heads of the forward [4,16,2048,64] (fp64 NumPy, {t_total:.1f} s)",
+        "cpu": model,
+        "blas": blas,
+        "visible_cpus": visible,
     }
+
+
+def cpu_baseline_others(budget_s=3.0, max_decode_heads=16):
+    """The oracle's split-K decode and backward on bounded samples of their
+    workloads (whole heads), for context next to the GPU figures."""
+    import torch
+
+    from exact_attention_05_amd.inputs import make_head, widen
+    from oracle import ref_bwd, ref_splitk_decode
+
+    _, cores, _, _ = _host_info()
+    out = {}
+    c = DEC
+    heads, t_total = 0, 0.0
+    while heads < min(c["B"] * c["H"], max_decode_heads) and t_total < budget_s:
+        b, h = divmod(heads, c["H"])
+        q = widen(make_head(0, "q", b, h, 1, c["d"], torch.bfloat16))
+        k, v = (widen(make_head(0, n, b, h, c["L"], c["d"], torch.bfloat16)) for n in ("k", "v"))
+        t0 = time.perf_counter()
+        ref_splitk_decode(q[None, None], k[None, None], v[None, None], 1.0 / math.sqrt(c["d"]), c["S"])
+        t_total += time.perf_counter() - t0
+        heads += 1
+    out["decode"] = {
+        "value": round(heads * 2 * c["L"] * c["d"] * 2 / t_total / 1e9, 4), "unit": "GB/s", "cores": cores,
+        "kind": "oracle", "sample": f"{heads} of {c['B'] * c['H']} heads of the decode [16,32,32768,128]/256 "
+                                    f"({t_total:.1f} s)"}
+    c = BWD
+    heads, t_total = 0, 0.0
+    while heads < c["B"] * c["H"] and t_total < budget_s:
+        b, h = divmod(heads, c["H"])
+        q, k, v, do = (widen(make_head(0, n, b, h, c["N"], c["d"], torch.bfloat16)) for n in ("q", "k", "v", "do"))
+        t0 = time.perf_counter()
+        ref_bwd(q[None, None], k[None, None], v[None, None], do[None, None], 1.0 / math.sqrt(c["d"]), True)
+        t_total += time.perf_counter() - t0
+        heads += 1
+    out["bwd"] = {
+        "value": round(heads * 2.5 * 2.0 * c["N"] ** 2 * c["d"] / t_total / 1e12, 6), "unit": "TFLOP/s",
+        "cores": cores, "kind": "oracle",
+        "sample": f"{heads} of {c['B'] * c['H']} heads of the causal backward [2,16,4096,64] ({t_total:.1f} s)"}
+    return out
 
 
 def main():
@@ -275,7 +337,9 @@ def main():
     t1.record(stream)
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    ms = {n: sum(e[n][0].elapsed_time(e[n][1]) for e in evs) / a.steps for n in names}
+    per = {n: sorted(e[n][0].elapsed_time(e[n][1]) for e in evs) for n in names}
+    ms = {n: sum(v) / len(v) for n, v in per.items()}
+    spread = {n: {"min_us": round(v[0] * 1e3, 2), "median_us": round(v[len(v) // 2] * 1e3, 2)} for n, v in per.items()}
 
     def rate(name, work, unit_div):
         return work / (ms[name] * 1e-3) / unit_div if name in ms else None
@@ -371,9 +435,12 @@ def main():
             "frac": round(f8 / PEAK_FP8_TFLOPS, 4),
             "traffic": _traffic("fwd_fp8_d64", ["fwd_fp8.hip", "common.h"]),
         }
+    out["per_launch"] = spread
     if not a.no_cpu_baseline and "fwd" in names:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline()
+        if "decode" in names and "bwd" in names:
+            out["cpu_baseline_other"] = cpu_baseline_others()
     print(json.dumps(out), flush=True)
 
 
