@@ -335,8 +335,11 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
 // rest across the row's lanes).  Pass 1 takes max|y| over the block; the
 // scale is 2^k, the smallest power of two with 448 2^k >= max|y| (k >= -126,
 // 1 for a zero block); pass 2 writes e4m3(y 2^-k), rounded to nearest even.
+// When the block spans at most NP passes of rows, its values stay in
+// registers after one read (all loads issued before any is used); NP = 0
+// reads the block twice.
 // ---------------------------------------------------------------------------
-template <int D, bool ROT>
+template <int D, bool ROT, int NP>
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const __bf16* __restrict__ X, const float* __restrict__ signs,
                                                         uint8_t* __restrict__ X8, float* __restrict__ scales,
                                                         int N, int block_rows, int nblk) {
@@ -396,14 +399,29 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const __bf16* __restrict
 
   // pass 1: max |y| over the block
   float amax = 0.f;
-  for (int p = 0; p < npass; ++p) {
-    const int r = r0 + p * RPP + tid / TPR;
-    float y[8];
-    const bool ok = r < r1;
-    load_row(ok ? r : r0, y);
-    if (ok) {
+  float held[NP > 0 ? NP : 1][8];
+  if constexpr (NP > 0) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[e]));
+    for (int p = 0; p < NP; ++p) {
+      const int r = r0 + p * RPP + tid / TPR;
+      if (p < npass) load_row(r < r1 ? r : r0, held[p]);
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+      if (p < npass && r0 + p * RPP + tid / TPR < r1) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(held[p][e]));
+      }
+  } else {
+    for (int p = 0; p < npass; ++p) {
+      const int r = r0 + p * RPP + tid / TPR;
+      float y[8];
+      const bool ok = r < r1;
+      load_row(ok ? r : r0, y);
+      if (ok) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[e]));
+      }
     }
   }
 #pragma unroll
@@ -424,22 +442,31 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const __bf16* __restrict
 
   // pass 2: codes
   uint8_t* X8h = X8 + (int64_t)bh * N * D;
-  for (int p = 0; p < npass; ++p) {
-    const int r = r0 + p * RPP + tid / TPR;
-    float y[8];
-    const bool ok = r < r1;
-    load_row(ok ? r : r0, y);
-    if (ok) {
-      uint32_t w[2];
+  auto store_row = [&](int r, const float (&y)[8]) __attribute__((always_inline)) {
+    uint32_t w[2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float z[4];
+    for (int h = 0; h < 2; ++h) {
+      float z[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) z[e] = fminf(fmaxf(ldexpf(y[4 * h + e], -k), -kP8Max), kP8Max);
-        int pw = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], 0, false);
-        w[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], pw, true);
-      }
-      *reinterpret_cast<u32x2*>(X8h + (int64_t)r * D + 8 * u) = u32x2{w[0], w[1]};
+      for (int e = 0; e < 4; ++e) z[e] = fminf(fmaxf(ldexpf(y[4 * h + e], -k), -kP8Max), kP8Max);
+      int pw = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], 0, false);
+      w[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], pw, true);
+    }
+    *reinterpret_cast<u32x2*>(X8h + (int64_t)r * D + 8 * u) = u32x2{w[0], w[1]};
+  };
+  if constexpr (NP > 0) {
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+      const int r = r0 + p * RPP + tid / TPR;
+      if (p < npass && r < r1) store_row(r, held[p]);
+    }
+  } else {
+    for (int p = 0; p < npass; ++p) {
+      const int r = r0 + p * RPP + tid / TPR;
+      float y[8];
+      const bool ok = r < r1;
+      load_row(ok ? r : r0, y);
+      if (ok) store_row(r, y);
     }
   }
 }
@@ -456,14 +483,26 @@ hipError_t run_fp8(const Fp8FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, bool ROT>
-hipError_t run_quant(const QuantArgs& a, hipStream_t s) {
+template <int D, bool ROT, int NP>
+hipError_t run_quant_np(const QuantArgs& a, hipStream_t s) {
   const int nblk = (a.N + a.block_rows - 1) / a.block_rows;
   const int64_t grid = (int64_t)a.B * a.H * nblk;
-  hipLaunchKernelGGL((quant_fp8_kernel<D, ROT>), dim3((unsigned)grid), dim3(256), 0, s,
+  hipLaunchKernelGGL((quant_fp8_kernel<D, ROT, NP>), dim3((unsigned)grid), dim3(256), 0, s,
                      static_cast<const __bf16*>(a.x), a.signs, static_cast<uint8_t*>(a.x8), a.scales, a.N,
                      a.block_rows, nblk);
   return hipGetLastError();
+}
+
+// passes of 256 / (D / 8) rows that one block needs: held in registers up to 4
+template <int D, bool ROT>
+hipError_t run_quant(const QuantArgs& a, hipStream_t s) {
+  constexpr int RPP = 256 / (D / 8);
+  const int rows = a.block_rows < a.N ? a.block_rows : a.N;
+  const int np = (rows + RPP - 1) / RPP;
+  if (np <= 1) return run_quant_np<D, ROT, 1>(a, s);
+  if (np <= 2) return run_quant_np<D, ROT, 2>(a, s);
+  if (np <= 4) return run_quant_np<D, ROT, 4>(a, s);
+  return run_quant_np<D, ROT, 0>(a, s);
 }
 
 }  // namespace
