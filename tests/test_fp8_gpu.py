@@ -227,3 +227,30 @@ def test_fp8_fwd_workload_sampled():
         O, LSE, R, RL = _oracle(*sub, bm, bn, 0.125, False)
         _assert_fp8_bar(f"O[{b},{h}]", widen(o[b:b + 1, h:h + 1]), O, R)
         _assert_fp8_lse(f"LSE[{b},{h}]", widen(lse[b:b + 1, h:h + 1]), LSE, RL)
+
+
+def test_fp8_fwd_offsets_beyond_2gib():
+    """E4M3 Q, K, V [1, H, 256, 64] spanning more than 2^31 bytes each (and
+    O more than 2^32): the first and last heads hold seeded data, the others
+    zeros with unit scales."""
+    N, d, bm, bn = 256, 64, 32, 64
+    H = (1 << 31) // (N * d) + 16
+    _say(f"fp8 fwd offsets beyond 2 GiB: [1,{H},{N},{d}]")
+    seed = 9
+    q8, k8, v8 = (torch.zeros((1, H, N, d), dtype=torch.uint8, device=DEV) for _ in range(3))
+    sq = torch.ones((1, H, N // bm), dtype=torch.float32, device=DEV)
+    sk = torch.ones((1, H, N // bn), dtype=torch.float32, device=DEV)
+    sv = torch.ones((1, H, N // bn), dtype=torch.float32, device=DEV)
+    ends = {}
+    for h in (0, H - 1):
+        one = _fp8_inputs(seed + h % 7, 1, 1, N, bm, bn)
+        ends[h] = one
+        for dst, src in ((q8, one[0]), (k8, one[1]), (v8, one[2]), (sq, one[3]), (sk, one[4]), (sv, one[5])):
+            dst[0, h].copy_(src[0, 0])
+    o, lse = attn_fwd_fp8(q8, k8, v8, sq, sk, sv, bm, bn, scale=0.125, causal=True)
+    torch.cuda.synchronize()
+    for h, one in ends.items():
+        O, LSE, R, RL = _oracle(*one, bm, bn, 0.125, True)
+        _assert_fp8_bar(f"O[{h}]", widen(o[0:1, h:h + 1]), O, R)
+        _assert_fp8_lse(f"LSE[{h}]", widen(lse[0:1, h:h + 1]), LSE, RL)
+    assert torch.count_nonzero(o[0, H // 2]) == 0

@@ -196,3 +196,30 @@ def test_long_causal_workload_sampled():
         O, LSE = ref_fwd(qh[rows], kh, vh, scale, True, q_pos=rows)
         assert_bar(f"O[{b},{h}]", widen(o[b, h, rows]), O, torch.bfloat16)
         assert_lse(f"LSE[{b},{h}]", widen(lse[b, h, rows]), LSE)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_offsets_beyond_2gib(d):
+    """Each tensor spans more than 2^31 bytes ([1, H, 256, d] bf16 with
+    H = 2^31 / (256 d 2) + 16): the first and last heads hold seeded N(0, 1)
+    data and are checked against the oracle, the others are zero (so their
+    output is zero and their LSE is ln 256)."""
+    N = 256
+    H = (1 << 31) // (N * d * 2) + 16
+    _say(f"fwd offsets beyond 2 GiB: [1,{H},{N},{d}]")
+    seed = 7
+    q, k, v = (torch.zeros((1, H, N, d), dtype=torch.bfloat16, device=DEV) for _ in range(3))
+    for h in (0, H - 1):
+        for t, n in ((q, "q"), (k, "k"), (v, "v")):
+            t[0, h].copy_(make_head(seed, n, 0, h, N, d, torch.bfloat16))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = attn_fwd(q, k, v, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    for h in (0, H - 1):
+        Q, K, V = (widen(make_head(seed, n, 0, h, N, d, torch.bfloat16)) for n in ("q", "k", "v"))
+        O, LSE = ref_fwd(Q[None, None], K[None, None], V[None, None], scale, True)
+        assert_bar(f"O[{h}]", widen(o[0, h]), O[0, 0], torch.bfloat16)
+        assert_lse(f"LSE[{h}]", widen(lse[0, h]), LSE[0, 0])
+    mid = H // 2
+    assert torch.count_nonzero(o[0, mid]) == 0
+    assert_lse("LSE[mid]", widen(lse[0, mid]), np.log(np.arange(1, N + 1, dtype=np.float64)))
