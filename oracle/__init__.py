@@ -47,4 +47,5 @@ from .attention_ref import (  # noqa: F401
     hadamard_rotate,
     quantize_fp8_blocks,
     ref_fwd_fp8,
+    ref_merge_lse,
 )

@@ -472,3 +472,30 @@ def ref_fwd_fp8(q8, k8, v8, sq, sk, sv, scale, causal=False, block_m=128, block_
     if tie_rel is not None:
         return O, LSE, R, RL
     return O, LSE
+
+
+# ---------------------------------------------------------------------------
+# Merging results over disjoint key sets (Ring Attention's per-step update)
+# ---------------------------------------------------------------------------
+
+def ref_merge_lse(o_a, lse_a, o_b, lse_b):
+    """Attention over keys A u B from the results over A and over B alone.
+
+    The partial-state merge of [FA1-vs-FA2] section 6 written for normalised
+    outputs: with L = log(e^LSE_a + e^LSE_b), O = e^(LSE_a - L) O_a +
+    e^(LSE_b - L) O_b and LSE = L.  This is the update each arriving K/V
+    shard makes in Ring Attention ([xuesongtap] section 5; [cnblogs]
+    section 3 scenario A).  A side with LSE = -inf (no keys) has weight 0;
+    both empty give O = 0, LSE = -inf.  o: [..., N, d]; lse: [..., N].
+    """
+    o_a, o_b = _f64(o_a), _f64(o_b)
+    la, lb = _f64(lse_a), _f64(lse_b)
+    m = np.maximum(la, lb)
+    base = np.where(np.isfinite(m), m, 0.0)
+    wa = np.where(np.isfinite(la), np.exp(la - base), 0.0)
+    wb = np.where(np.isfinite(lb), np.exp(lb - base), 0.0)
+    tot = wa + wb
+    safe = np.where(tot > 0, tot, 1.0)
+    O = (wa[..., None] * o_a + wb[..., None] * o_b) / safe[..., None]
+    L = np.where(tot > 0, base + np.log(safe), NEG_INF)
+    return O, L

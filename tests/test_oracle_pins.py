@@ -644,6 +644,63 @@ def test_hadamard_rotation_helps_outlier_features():
 
 
 # ---------------------------------------------------------------------------
+# Merging results over disjoint key sets ([FA1-vs-FA2] section 6)
+# ---------------------------------------------------------------------------
+
+def _fwd_on_keys(q, k, v, scale, keys):
+    """Plain attention of every query over the key subset `keys` (no mask)."""
+    return ar.ref_fwd(q, k[..., keys, :], v[..., keys, :], scale)
+
+
+def test_merge_of_key_subsets_is_attention_over_their_union():
+    q, k, v = _rand((2, 3, 9, 5), 90), _rand((2, 3, 13, 5), 91), _rand((2, 3, 13, 5), 92)
+    perm = np.random.default_rng(93).permutation(13)
+    A, Bk = perm[:6], perm[6:]
+    Oa, La = _fwd_on_keys(q, k, v, 0.7, A)
+    Ob, Lb = _fwd_on_keys(q, k, v, 0.7, Bk)
+    O, L = ar.ref_merge_lse(Oa, La, Ob, Lb)
+    O2, L2 = ar.ref_fwd(q, k, v, 0.7)
+    np.testing.assert_allclose(O, O2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(L, L2, rtol=1e-13)
+
+
+def test_merge_ring_of_causal_shards_is_causal_attention():
+    """G query/key shards of a causal problem: shard i of the queries sees
+    the diagonal block causally and blocks j < i fully; merging those partial
+    results in ring order gives causal attention over the whole sequence."""
+    N, G, S = 24, 4, 6
+    q, k, v = _rand((1, 2, N, 4), 94), _rand((1, 2, N, 4), 95), _rand((1, 2, N, 4), 96)
+    O2, L2 = ar.ref_fwd(q, k, v, 0.5, causal=True)
+    for i in range(G):
+        rows = slice(i * S, (i + 1) * S)
+        O, L = ar.ref_fwd(q[..., rows, :], k[..., rows, :], v[..., rows, :], 0.5, causal=True)
+        for j in range(i - 1, -1, -1):
+            cols = slice(j * S, (j + 1) * S)
+            Oj, Lj = ar.ref_fwd(q[..., rows, :], k[..., cols, :], v[..., cols, :], 0.5)
+            O, L = ar.ref_merge_lse(O, L, Oj, Lj)
+        np.testing.assert_allclose(O, O2[..., rows, :], rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(L, L2[..., rows], rtol=1e-13)
+
+
+def test_merge_identity_and_symmetry():
+    o, l = _rand((3, 4), 97), _rand((3,), 98)
+    o2, l2 = _rand((3, 4), 99), _rand((3,), 100)
+    empty_o, empty_l = np.zeros((3, 4)), np.full(3, -np.inf)
+    O, L = ar.ref_merge_lse(o, l, empty_o, empty_l)
+    assert np.array_equal(O, o) and np.array_equal(L, l)
+    O, L = ar.ref_merge_lse(empty_o, empty_l, empty_o, empty_l)
+    assert np.all(O == 0) and np.all(L == -np.inf)
+    Oab, Lab = ar.ref_merge_lse(o, l, o2, l2)
+    Oba, Lba = ar.ref_merge_lse(o2, l2, o, l)
+    np.testing.assert_allclose(Oab, Oba, rtol=1e-15)
+    np.testing.assert_allclose(Lab, Lba, rtol=1e-15)
+    # equal LSEs: the plain average, and LSE + ln 2
+    O, L = ar.ref_merge_lse(o, l, o2, l)
+    np.testing.assert_allclose(O, 0.5 * (o + o2), rtol=1e-15)
+    np.testing.assert_allclose(L, l + np.log(2.0), rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------
 # Mutation tests: plausible oracle mistakes must fail the pins above
 # ---------------------------------------------------------------------------
 
@@ -728,6 +785,14 @@ def test_mutant_fp8_v_scale_mixup_fails_bound(monkeypatch):
     monkeypatch.setattr(ar, "_rows_of_blocks", bad_rows)
     with pytest.raises(AssertionError):
         test_fp8_forward_error_within_p_rounding_bound(False)
+
+
+def test_mutant_lse_merge_without_weights_fails_union_pin(monkeypatch):
+    """Averaging the two partial outputs (ignoring their LSEs) must break the
+    union pin."""
+    monkeypatch.setattr(ar, "ref_merge_lse", lambda oa, la, ob, lb: (0.5 * (oa + ob), np.logaddexp(la, lb)))
+    with pytest.raises(AssertionError):
+        test_merge_of_key_subsets_is_attention_over_their_union()
 
 
 def test_oracle_exports():
