@@ -10,6 +10,10 @@ inputs:
   * split-K decode over a paged cache holding the same K/V cache in 16-token
     blocks scattered over the pool by a random block table (reported only;
     its output must equal the dense decode's bit for bit)
+  * one GPU's share of an 8-GPU Ring Attention over the long causal
+    forward's inputs (the last GPU: its causal diagonal shard, then seven
+    earlier 1024-token K/V shards, each forward merged into its running
+    result; reported only)
   * forward on FP8 (E4M3) storage of the headline Q, K, V (per-block
     power-of-two scales: Q per 128 rows, K and V per 64; quantised before the
     timed region), non-causal (reported only)
@@ -41,6 +45,7 @@ DEC = dict(B=16, H=32, L=32768, d=128, S=256)
 DEC_PAGED = dict(DEC, block_size=16)
 BWD = dict(B=2, H=16, N=4096, d=64, causal=True)
 FP8_BLOCKS = (128, 64)  # rows per scale: Q, then K and V
+RING_G = 8  # GPUs in the ring whose per-GPU share is timed
 
 
 def fwd_flops(c):
@@ -197,13 +202,13 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--only", default="",
-                    help="comma-separated subset of fwd,decode,bwd,fwd_long,decode_paged,fwd_fp8 to run "
+                    help="comma-separated subset of fwd,decode,bwd,fwd_long,decode_paged,fwd_fp8,ring to run "
                          "(profiling passes)")
     a = ap.parse_args()
-    parts = ["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long"]) + ["decode_paged", "fwd_fp8"]
+    parts = ["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long", "ring"]) + ["decode_paged", "fwd_fp8"]
     if a.only:
         parts = [p for p in a.only.split(",") if p]
-        bad = [p for p in parts if p not in ("fwd", "decode", "bwd", "fwd_long", "decode_paged", "fwd_fp8")]
+        bad = [p for p in parts if p not in ("fwd", "decode", "bwd", "fwd_long", "decode_paged", "fwd_fp8", "ring")]
         if bad:
             ap.error(f"unknown --only parts {bad}")
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -214,7 +219,7 @@ def main():
     import torch
 
     from exact_attention_05_amd import (attn_bwd, attn_fwd, attn_fwd_fp8, attn_fwd_splitk_decode,
-                                        attn_fwd_splitk_decode_paged, attn_quantize_fp8)
+                                        attn_fwd_splitk_decode_paged, attn_merge, attn_quantize_fp8)
     from exact_attention_05_amd.binding import attn_bwd_workspace_bytes, attn_decode_workspace_bytes
     from exact_attention_05_amd.inputs import make_block_table, make_tensor
 
@@ -276,11 +281,20 @@ def main():
         bgq, bgk, bgv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
         bws = torch.empty(attn_bwd_workspace_bytes(c["B"], c["H"], c["N"]) // 4, dtype=torch.float32,
                           device=dev)
-    if "fwd_long" in parts:
+    if "fwd_long" in parts or "ring" in parts:
         c = FWD_LONG
         lq, lk, lv = mk(0, ("q", "k", "v"), c["B"], c["H"], c["N"], c["d"], c["input_scale"])
         lo = torch.empty_like(lq)
         llse = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device=dev)
+    if "ring" in parts:
+        S = FWD_LONG["N"] // RING_G
+        sh = lambda t, j: t[:, :, j * S:(j + 1) * S].contiguous()
+        me = RING_G - 1  # the last GPU: the most shards below its diagonal
+        rq = sh(lq, me)
+        rk = [sh(lk, j) for j in range(RING_G)]
+        rv = [sh(lv, j) for j in range(RING_G)]
+        ro, rl = torch.empty_like(rq), torch.empty(rq.shape[:3], dtype=torch.float32, device=dev)
+        rpo, rpl = torch.empty_like(rq), torch.empty_like(rl)
     torch.cuda.synchronize()
     print("bench: inputs resident", file=sys.stderr, flush=True)
 
@@ -311,6 +325,13 @@ def main():
             ev["fwd_long"][0].record(stream)
             attn_fwd(lq, lk, lv, causal=True, out=lo, lse=llse)
             ev["fwd_long"][1].record(stream)
+        if "ring" in names:
+            ev["ring"][0].record(stream)
+            attn_fwd(rq, rk[me], rv[me], causal=True, out=ro, lse=rl)
+            for j in range(me - 1, -1, -1):
+                attn_fwd(rq, rk[j], rv[j], causal=False, out=rpo, lse=rpl)
+                attn_merge(ro, rl, rpo, rpl, out=ro, lse=rl)
+            ev["ring"][1].record(stream)
         if "fwd_fp8" in names:
             ev["fwd_fp8"][0].record(stream)
             attn_fwd_fp8(q8, k8, v8, sq8, sk8, sv8, FP8_BLOCKS[0], FP8_BLOCKS[1], causal=False, out=o8, lse=lse8)
@@ -368,7 +389,7 @@ def main():
                         "bf16 q[16,32,1,128] x KV[16,32,32768,128], 256 chunks; backward bf16 [2,16,4096,64] "
                         "causal; forward bf16 [2,32,8192,128] causal (reported); the same decode over a "
                         "paged cache of 16-token blocks (reported); the headline forward on FP8 E4M3 storage "
-                        "(reported)",
+                        "(reported); one GPU's share of an 8-GPU ring over the long causal forward (reported)",
             "global_batch": FWD["B"],
             "seq_len": FWD["N"],
             "parallelism": "single GPU",
@@ -422,6 +443,12 @@ def main():
             "frac": round(pg / PEAK_HBM_GBPS, 4),
             "traffic": _traffic("decode_paged_d128", ["decode.hip", "common.h"]),
         }
+    if "ring" in ms:
+        c = FWD_LONG
+        S = c["N"] // RING_G
+        ring_flops = 4.0 * c["B"] * c["H"] * S * S * c["d"] * ((RING_G - 1) + 0.5)
+        out["ring_share_tflops"] = round(ring_flops / (ms["ring"] * 1e-3) / 1e12, 3)
+        out["ring_share_us"] = round(ms["ring"] * 1e3, 2)
     if "fwd_fp8" in ms:
         f8 = rate("fwd_fp8", fwd_flops(FWD), 1e12)
         out["fwd_fp8_tflops"] = round(f8, 3)

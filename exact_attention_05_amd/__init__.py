@@ -13,6 +13,7 @@ __all__ = [
     "attn_bwd",
     "attn_quantize_fp8",
     "attn_fwd_fp8",
+    "attn_merge",
     "attn_decode_workspace_bytes",
     "attn_bwd_workspace_bytes",
     "attn_status_string",

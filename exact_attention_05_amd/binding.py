@@ -67,6 +67,8 @@ def _load():
     lib.attn_quantize_fp8.argtypes = [vp, vp, vp, vp, ci, ci, ci, ci, ci, vp]
     lib.attn_fwd_fp8.restype = ci
     lib.attn_fwd_fp8.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.attn_merge.restype = ci
+    lib.attn_merge.argtypes = [vp, vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, vp]
     lib.attn_bwd_workspace_bytes.restype = sz
     lib.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci]
     lib.attn_bwd.restype = ci
@@ -275,6 +277,33 @@ def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, block_m, block_n, scale=
                               _ptr(lse), B, H, N, d, int(block_m), int(block_n), scale, int(bool(causal)),
                               _stream(dev))
     _check(st, "attn_fwd_fp8")
+    return out, lse
+
+
+def attn_merge(o_a, lse_a, o_b, lse_b, out=None, lse=None):
+    """(O, LSE) over the union of two disjoint key sets from the results over
+    each: O = e^(LSE_a - L) O_a + e^(LSE_b - L) O_b, L = log(e^LSE_a + e^LSE_b).
+
+    o_* [B, H, N, d], lse_* [B, H, N] fp32; ``out``/``lse`` may be o_a/lse_a
+    (or o_b/lse_b) to merge in place.  Returns (out, lse).
+    """
+    B, H, N, d = o_a.shape
+    dev = o_a.device
+    _check_bhnd("o_a", o_a, (B, H, N, d), o_a.dtype, dev)
+    _check_bhnd("o_b", o_b, (B, H, N, d), o_a.dtype, dev)
+    for name, t in (("lse_a", lse_a), ("lse_b", lse_b)):
+        _check_bhnd(name, t, (B, H, N), torch.float32, dev)
+    if out is None:
+        out = torch.empty_like(o_a)
+    else:
+        _check_bhnd("out", out, (B, H, N, d), o_a.dtype, dev)
+    if lse is None:
+        lse = torch.empty_like(lse_a)
+    else:
+        _check_bhnd("lse", lse, (B, H, N), torch.float32, dev)
+    st = _load().attn_merge(_ptr(o_a), _ptr(lse_a), _ptr(o_b), _ptr(lse_b), _ptr(out), _ptr(lse), B, H, N, d,
+                            _dtype_code(o_a), _stream(dev))
+    _check(st, "attn_merge")
     return out, lse
 
 

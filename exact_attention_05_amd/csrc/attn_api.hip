@@ -143,6 +143,21 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const f
   return from_hip(attn::launch_fwd_fp8(a, static_cast<hipStream_t>(stream)));
 }
 
+attn_status attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b, void* o, float* lse,
+                       int B, int H, int N, int d, attn_dtype dtype, void* stream) {
+  if (B < 1 || H < 1 || N < 1 || N > (1 << 24) || d < 1) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * H * N > ((int64_t)1 << 40)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (!tensor_ok(o_a) || !tensor_ok(o_b) || !tensor_ok(o)) return ATTN_ERR_INVALID_ARG;
+  for (const float* p : {lse_a, lse_b, static_cast<const float*>(lse)})
+    if (p == nullptr || !aligned(p, 4)) return ATTN_ERR_INVALID_ARG;
+  if (d != 64 && d != 128) return ATTN_ERR_UNSUPPORTED;
+  const int64_t rows = (int64_t)B * H * N;
+  if ((rows + (256 / (d / 8)) - 1) / (256 / (d / 8)) > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  attn::MergeArgs a{o_a, lse_a, o_b, lse_b, o, lse, B, H, N, d, dtype == ATTN_BF16};
+  return from_hip(attn::launch_merge(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t attn_bwd_workspace_bytes(int B, int H, int N) {
   if (B < 1 || H < 1 || N < 1) return 0;
   return (size_t)B * (size_t)H * (size_t)N * 24;

@@ -75,6 +75,21 @@ struct QuantArgs {
 
 hipError_t launch_quantize_fp8(const QuantArgs& a, hipStream_t s);
 
+// Merge of two results over disjoint key sets; o/lse may alias o_a/lse_a or
+// o_b/lse_b.
+struct MergeArgs {
+  const void* o_a;
+  const float* lse_a;
+  const void* o_b;
+  const float* lse_b;
+  void* o;
+  float* lse;
+  int B, H, N, d;
+  bool bf16;
+};
+
+hipError_t launch_merge(const MergeArgs& a, hipStream_t s);
+
 struct BwdArgs {
   const void* q;
   const void* k;

@@ -16,6 +16,8 @@
  *   attn_quantize_fp8, attn_fwd_fp8
  *                           FP8 (E4M3) storage with per-block scales, and
  *                           the forward on it.
+ *   attn_merge              (O, LSE) over two disjoint key sets -> over
+ *                           their union (Ring Attention's per-shard update).
  *
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers, owned by the caller.  The
@@ -232,6 +234,33 @@ attn_status attn_quantize_fp8(const void* x, const float* signs, void* x8, float
 attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
                          const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H,
                          int N, int d, int block_m, int block_n, float scale, int causal, void* stream);
+
+/*
+ * attn_merge -- combine attention results over two disjoint key sets.
+ *
+ * Given (O_a, LSE_a) over keys A and (O_b, LSE_b) over keys B for the same
+ * query rows, writes the result over A u B: per row,
+ *     L = log(e^LSE_a + e^LSE_b),
+ *     O = e^(LSE_a - L) O_a + e^(LSE_b - L) O_b,   LSE = L,
+ * the partial-state merge of "FlashAttention 1 和 FlashAttention 2 的区别",
+ * section 6, for normalised outputs.  It is the update a GPU makes for each
+ * K/V shard that reaches it in Ring Attention ("FlashAttention",
+ * xuesongtap.github.io, section 5): attn_fwd on (its queries, the arriving
+ * shard) -- causal on the diagonal shard, non-causal below it -- then this
+ * merge into its running result.  A side with LSE = -inf contributes nothing
+ * (its O is not read); both empty give O = 0, LSE = -inf.
+ *
+ *   o_a, o_b, o  : [B, H, N, d] in `dtype`;  lse_a, lse_b, lse: [B, H, N] fp32
+ *   o may be o_a or o_b and lse may be lse_a or lse_b (in place); other
+ *   overlaps are not allowed.
+ *
+ * Supported: ATTN_BF16 and ATTN_F32 with d in {64, 128}.
+ * Errors: ATTN_ERR_INVALID_ARG for NULL or misaligned pointers (o's 16
+ * bytes, lse's 4) or sizes out of range; ATTN_ERR_UNSUPPORTED for another d.
+ */
+attn_status attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
+                       void* o, float* lse, int B, int H, int N, int d, attn_dtype dtype,
+                       void* stream);
 
 /*
  * Workspace size in bytes that attn_bwd needs: 24 bytes per query row

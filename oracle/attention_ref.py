@@ -485,8 +485,9 @@ def ref_merge_lse(o_a, lse_a, o_b, lse_b):
     outputs: with L = log(e^LSE_a + e^LSE_b), O = e^(LSE_a - L) O_a +
     e^(LSE_b - L) O_b and LSE = L.  This is the update each arriving K/V
     shard makes in Ring Attention ([xuesongtap] section 5; [cnblogs]
-    section 3 scenario A).  A side with LSE = -inf (no keys) has weight 0;
-    both empty give O = 0, LSE = -inf.  o: [..., N, d]; lse: [..., N].
+    section 3 scenario A).  A side with LSE = -inf (no keys) has weight 0
+    and contributes nothing whatever its O holds; both empty give O = 0,
+    LSE = -inf.  o: [..., N, d]; lse: [..., N].
     """
     o_a, o_b = _f64(o_a), _f64(o_b)
     la, lb = _f64(lse_a), _f64(lse_b)
@@ -496,6 +497,8 @@ def ref_merge_lse(o_a, lse_a, o_b, lse_b):
     wb = np.where(np.isfinite(lb), np.exp(lb - base), 0.0)
     tot = wa + wb
     safe = np.where(tot > 0, tot, 1.0)
-    O = (wa[..., None] * o_a + wb[..., None] * o_b) / safe[..., None]
+    ta = np.where(wa[..., None] > 0, wa[..., None] * o_a, 0.0)
+    tb = np.where(wb[..., None] > 0, wb[..., None] * o_b, 0.0)
+    O = (ta + tb) / safe[..., None]
     L = np.where(tot > 0, base + np.log(safe), NEG_INF)
     return O, L

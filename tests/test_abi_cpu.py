@@ -30,7 +30,7 @@ def _declared_functions():
 def test_header_declares_the_boundary():
     names = _declared_functions()
     for n in ("attn_fwd", "attn_fwd_splitk_decode", "attn_fwd_splitk_decode_paged", "attn_bwd",
-              "attn_quantize_fp8", "attn_fwd_fp8",
+              "attn_quantize_fp8", "attn_fwd_fp8", "attn_merge",
               "attn_decode_workspace_bytes",
               "attn_bwd_workspace_bytes", "attn_status_string", "attn_abi_version"):
         assert n in names
@@ -197,6 +197,27 @@ def test_fwd_fp8_validation():
     assert call(N=0) == INVALID
     assert call(sc=0.0) == INVALID
     assert call(d=128) == UNSUPPORTED
+
+
+def test_merge_validation():
+    lib = _lib()
+    f = lib.attn_merge
+    S4 = ctypes.c_void_p(0x10004)
+    base = dict(oa=P, la=S4, ob=P, lb=S4, o=P, lse=S4, B=1, H=2, N=100, d=64, dt=BF16)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["oa"], a["la"], a["ob"], a["lb"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"], a["dt"], None)
+
+    assert call(oa=NULL) == INVALID
+    assert call(ob=MIS) == INVALID
+    assert call(lse=NULL) == INVALID
+    assert call(lb=ctypes.c_void_p(0x10002)) == INVALID
+    assert call(N=0) == INVALID
+    assert call(N=(1 << 24) + 1) == INVALID
+    assert call(dt=5) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(d=32, dt=F32) == UNSUPPORTED
 
 
 def test_bwd_validation():

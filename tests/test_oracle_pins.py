@@ -690,6 +690,9 @@ def test_merge_identity_and_symmetry():
     assert np.array_equal(O, o) and np.array_equal(L, l)
     O, L = ar.ref_merge_lse(empty_o, empty_l, empty_o, empty_l)
     assert np.all(O == 0) and np.all(L == -np.inf)
+    with np.errstate(invalid="ignore"):
+        O, L = ar.ref_merge_lse(o, l, np.full((3, 4), np.nan), empty_l)  # an empty side's O is never read
+    assert np.array_equal(O, o) and np.array_equal(L, l)
     Oab, Lab = ar.ref_merge_lse(o, l, o2, l2)
     Oba, Lba = ar.ref_merge_lse(o2, l2, o, l)
     np.testing.assert_allclose(Oab, Oba, rtol=1e-15)
