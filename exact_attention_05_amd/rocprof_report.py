@@ -103,21 +103,48 @@ def src_sha(names):
     return h.hexdigest()[:16]
 
 
+def kernel_dispatch_stats(d):
+    """[(name, grid, calls, avg_ns, min_ns, max_ns, pct)] from the --kernel-trace
+    CSV, one row per kernel and grid size (one kernel can serve several
+    workloads in one run), or None when the directory holds no trace."""
+    try:
+        path = _find(d, "kernel_trace.csv")
+    except FileNotFoundError:
+        return None
+    groups = collections.defaultdict(list)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            groups[(r["Kernel_Name"], grid)].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    total = sum(sum(v) for v in groups.values()) or 1
+    rows = [(name, grid, len(v), sum(v) / len(v), min(v), max(v), 100.0 * sum(v) / total)
+            for (name, grid), v in groups.items()]
+    rows.sort(key=lambda r: -r[2] * r[3])
+    return rows
+
+
 def cmd_stats(a):
-    rows = kernel_stats(a.dir)
-    work = {}
+    rows = kernel_dispatch_stats(a.dir)
+    if rows is None:
+        rows = [(name, None, calls, avg, mn, mx, pct) for name, calls, avg, mn, mx, pct in kernel_stats(a.dir)]
+    work = []
     for spec in a.work or []:
-        # REGEX=AMOUNT:UNIT with UNIT in {flop, flop8, byte} (flop8: FP8 products)
+        # REGEX[@GRID]=AMOUNT:UNIT with UNIT in {flop, flop8, byte} (flop8: FP8
+        # products); GRID (work-items per launch) picks one workload of a kernel
         rx, rest = spec.rsplit("=", 1)
+        grid = None
+        if "@" in rx:
+            rx, g = rx.rsplit("@", 1)
+            grid = int(g)
         amt, unit = rest.split(":")
-        work[rx] = (float(amt), unit)
+        work.append((rx, grid, float(amt), unit))
     lines = [f"# {a.title}", "", "Command (GPU box, repo root):", "", "```", a.cmd, "```", ""]
-    lines.append("| kernel | calls | average (us) | min (us) | max (us) | share | achieved vs peak |")
-    lines.append("|---|---|---|---|---|---|---|")
-    for name, calls, avg, mn, mx, pct in rows:
+    lines.append("| kernel | grid (work-items) | calls | average (us) | min (us) | max (us) | share | achieved vs peak |")
+    lines.append("|---|---|---|---|---|---|---|---|")
+    for name, grid, calls, avg, mn, mx, pct in rows:
         ach = ""
-        for rx, (amt, unit) in work.items():
-            if re.search(rx, name):
+        for rx, wgrid, amt, unit in work:
+            if re.search(rx, name) and (wgrid is None or wgrid == grid):
                 if unit in ("flop", "flop8"):
                     t = amt / (avg * 1e-9) / 1e12
                     peak, kind = (PEAK_FP8_TFLOPS, "FP8") if unit == "flop8" else (PEAK_BF16_TFLOPS, "bf16")
@@ -125,7 +152,8 @@ def cmd_stats(a):
                 else:
                     g = amt / (avg * 1e-9) / 1e9
                     ach = f"{g:.1f} GB/s = {100 * g / PEAK_HBM_GBPS:.1f}% of HBM"
-        lines.append(f"| `{short_name(name)}` | {calls} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | "
+        gtxt = "" if grid is None else str(grid)
+        lines.append(f"| `{short_name(name)}` | {gtxt} | {calls} | {avg / 1e3:.1f} | {mn / 1e3:.1f} | {mx / 1e3:.1f} | "
                      f"{pct:.1f}% | {ach} |")
     text = "\n".join(lines) + "\n"
     if a.out:
@@ -211,7 +239,7 @@ def main(argv=None):
     s.add_argument("--title", required=True)
     s.add_argument("--cmd", required=True)
     s.add_argument("--out")
-    s.add_argument("--work", action="append", help="REGEX=AMOUNT:flop|flop8|byte per launch")
+    s.add_argument("--work", action="append", help="REGEX[@GRID]=AMOUNT:flop|flop8|byte per launch")
     s.set_defaults(fn=cmd_stats)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
