@@ -17,6 +17,8 @@ inputs:
   * forward on FP8 (E4M3) storage of the headline Q, K, V (per-block
     power-of-two scales: Q per 128 rows, K and V per 64; quantised before the
     timed region), non-causal (reported only)
+  * the same backward with dQ accumulated by fp32 atomic adds in the dK/dV
+    pass (zero fill + preprocess + dK/dV/dQ + dQ scaling; reported only)
 
 `value` is the forward's TFLOP/s (4*B*H*N^2*d per call) from HIP events
 around its launch on the launch stream, averaged over the timed steps.
@@ -202,13 +204,16 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--only", default="",
-                    help="comma-separated subset of fwd,decode,bwd,fwd_long,decode_paged,fwd_fp8,ring to run "
+                    help="comma-separated subset of fwd,decode,bwd,fwd_long,decode_paged,fwd_fp8,ring,bwd_atomic "
+                         "to run "
                          "(profiling passes)")
     a = ap.parse_args()
-    parts = ["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long", "ring"]) + ["decode_paged", "fwd_fp8"]
+    parts = (["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long", "ring"])
+             + ["decode_paged", "fwd_fp8", "bwd_atomic"])
     if a.only:
         parts = [p for p in a.only.split(",") if p]
-        bad = [p for p in parts if p not in ("fwd", "decode", "bwd", "fwd_long", "decode_paged", "fwd_fp8", "ring")]
+        bad = [p for p in parts if p not in ("fwd", "decode", "bwd", "fwd_long", "decode_paged", "fwd_fp8", "ring",
+                                             "bwd_atomic")]
         if bad:
             ap.error(f"unknown --only parts {bad}")
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -218,9 +223,10 @@ def main():
 
     import torch
 
-    from exact_attention_05_amd import (attn_bwd, attn_fwd, attn_fwd_fp8, attn_fwd_splitk_decode,
+    from exact_attention_05_amd import (attn_bwd, attn_bwd_atomic_dq, attn_fwd, attn_fwd_fp8, attn_fwd_splitk_decode,
                                         attn_fwd_splitk_decode_paged, attn_merge, attn_quantize_fp8)
-    from exact_attention_05_amd.binding import attn_bwd_workspace_bytes, attn_decode_workspace_bytes
+    from exact_attention_05_amd.binding import (attn_bwd_atomic_workspace_bytes, attn_bwd_workspace_bytes,
+                                                attn_decode_workspace_bytes)
     from exact_attention_05_amd.inputs import make_block_table, make_tensor
 
     dev = torch.device("cuda:0")
@@ -274,13 +280,17 @@ def main():
         del xq, xk, xv
         o8 = torch.empty((c["B"], c["H"], c["N"], c["d"]), dtype=bf16, device=dev)
         lse8 = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device=dev)
-    if "bwd" in parts:
+    if "bwd" in parts or "bwd_atomic" in parts:
         c = BWD
         bq, bk, bv, bdo = mk(0, ("q", "k", "v", "do"), c["B"], c["H"], c["N"], c["d"])
         bo, blse = attn_fwd(bq, bk, bv, causal=True)
         bgq, bgk, bgv = torch.empty_like(bq), torch.empty_like(bk), torch.empty_like(bv)
         bws = torch.empty(attn_bwd_workspace_bytes(c["B"], c["H"], c["N"]) // 4, dtype=torch.float32,
                           device=dev)
+    if "bwd_atomic" in parts:
+        c = BWD
+        aws = torch.empty(attn_bwd_atomic_workspace_bytes(c["B"], c["H"], c["N"], c["d"]) // 4,
+                          dtype=torch.float32, device=dev)
     if "fwd_long" in parts or "ring" in parts:
         c = FWD_LONG
         lq, lk, lv = mk(0, ("q", "k", "v"), c["B"], c["H"], c["N"], c["d"], c["input_scale"])
@@ -336,6 +346,10 @@ def main():
             ev["fwd_fp8"][0].record(stream)
             attn_fwd_fp8(q8, k8, v8, sq8, sk8, sv8, FP8_BLOCKS[0], FP8_BLOCKS[1], causal=False, out=o8, lse=lse8)
             ev["fwd_fp8"][1].record(stream)
+        if "bwd_atomic" in names:
+            ev["bwd_atomic"][0].record(stream)
+            attn_bwd_atomic_dq(bq, bk, bv, bo, bdo, blse, causal=True, dq=bgq, dk=bgk, dv=bgv, workspace=aws)
+            ev["bwd_atomic"][1].record(stream)
         if "decode_paged" in names:
             ev["decode_paged"][0].record(stream)
             attn_fwd_splitk_decode_paged(dq_, pk, pv, ptab, plens, DEC["S"], out=po, lse=plse, workspace=pws)
@@ -389,7 +403,8 @@ def main():
                         "bf16 q[16,32,1,128] x KV[16,32,32768,128], 256 chunks; backward bf16 [2,16,4096,64] "
                         "causal; forward bf16 [2,32,8192,128] causal (reported); the same decode over a "
                         "paged cache of 16-token blocks (reported); the headline forward on FP8 E4M3 storage "
-                        "(reported); one GPU's share of an 8-GPU ring over the long causal forward (reported)",
+                        "(reported); one GPU's share of an 8-GPU ring over the long causal forward (reported); "
+                        "the backward with atomic dQ (reported)",
             "global_batch": FWD["B"],
             "seq_len": FWD["N"],
             "parallelism": "single GPU",
@@ -462,6 +477,9 @@ def main():
             "frac": round(f8 / PEAK_FP8_TFLOPS, 4),
             "traffic": _traffic("fwd_fp8_d64", ["fwd_fp8.hip", "common.h"]),
         }
+    if "bwd_atomic" in ms:
+        out["bwd_atomic_tflops"] = round(rate("bwd_atomic", 2.5 * fwd_flops(BWD), 1e12), 3)
+        out["bwd_atomic_us"] = round(ms["bwd_atomic"] * 1e3, 2)
     out["per_launch"] = spread
     if not a.no_cpu_baseline and "fwd" in names:
         print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)

@@ -11,11 +11,13 @@ __all__ = [
     "attn_fwd_splitk_decode",
     "attn_fwd_splitk_decode_paged",
     "attn_bwd",
+    "attn_bwd_atomic_dq",
     "attn_quantize_fp8",
     "attn_fwd_fp8",
     "attn_merge",
     "attn_decode_workspace_bytes",
     "attn_bwd_workspace_bytes",
+    "attn_bwd_atomic_workspace_bytes",
     "attn_status_string",
     "AttnError",
     "library_path",

@@ -73,6 +73,10 @@ def _load():
     lib.attn_bwd_workspace_bytes.argtypes = [ci, ci, ci]
     lib.attn_bwd.restype = ci
     lib.attn_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.attn_bwd_atomic_workspace_bytes.restype = sz
+    lib.attn_bwd_atomic_workspace_bytes.argtypes = [ci, ci, ci, ci]
+    lib.attn_bwd_atomic_dq.restype = ci
+    lib.attn_bwd_atomic_dq.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, cf, ci, vp]
     _lib = lib
     return lib
 
@@ -321,12 +325,26 @@ def attn_bwd_workspace_bytes(B, H, N):
     return int(_load().attn_bwd_workspace_bytes(B, H, N))
 
 
+def attn_bwd_atomic_workspace_bytes(B, H, N, d):
+    return int(_load().attn_bwd_atomic_workspace_bytes(B, H, N, d))
+
+
 def attn_bwd(q, k, v, o, dO, lse, scale=None, causal=False, dq=None, dk=None, dv=None, workspace=None):
     """dQ, dK, dV of attention from the forward's saved O and LSE.
 
     Returns (dq, dk, dv, workspace); the workspace starts with D = rowsum(dO o O)
     (B*H*N fp32 values).
     """
+    return _bwd_call("attn_bwd", q, k, v, o, dO, lse, scale, causal, dq, dk, dv, workspace)
+
+
+def attn_bwd_atomic_dq(q, k, v, o, dO, lse, scale=None, causal=False, dq=None, dk=None, dv=None, workspace=None):
+    """As attn_bwd, with dQ accumulated by fp32 atomic adds in the dK/dV pass
+    (dq is not bitwise reproducible).  Returns (dq, dk, dv, workspace)."""
+    return _bwd_call("attn_bwd_atomic_dq", q, k, v, o, dO, lse, scale, causal, dq, dk, dv, workspace)
+
+
+def _bwd_call(entry, q, k, v, o, dO, lse, scale, causal, dq, dk, dv, workspace):
     B, H, N, d = q.shape
     dev = q.device
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("dO", dO)):
@@ -336,11 +354,14 @@ def attn_bwd(q, k, v, o, dO, lse, scale=None, causal=False, dq=None, dk=None, dv
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    need = attn_bwd_workspace_bytes(B, H, N)
+    if entry == "attn_bwd":
+        need = attn_bwd_workspace_bytes(B, H, N)
+    else:
+        need = attn_bwd_atomic_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
-    st = _load().attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
-                          _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
-                          B, H, N, d, _dtype_code(q), scale, int(bool(causal)), _stream(dev))
-    _check(st, "attn_bwd")
+    st = getattr(_load(), entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
+                                 _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                 B, H, N, d, _dtype_code(q), scale, int(bool(causal)), _stream(dev))
+    _check(st, entry)
     return dq, dk, dv, workspace

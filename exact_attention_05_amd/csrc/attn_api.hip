@@ -179,4 +179,31 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
   return from_hip(attn::launch_bwd_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
+static size_t bwd_terms_bytes_aligned(int B, int H, int N) {
+  return (attn_bwd_workspace_bytes(B, H, N) + 255) & ~(size_t)255;
+}
+
+size_t attn_bwd_atomic_workspace_bytes(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return 0;
+  return bwd_terms_bytes_aligned(B, H, N) + (size_t)B * (size_t)H * (size_t)N * (size_t)d * 4;
+}
+
+attn_status attn_bwd_atomic_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                               const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                               size_t workspace_bytes, int B, int H, int N, int d, attn_dtype dtype,
+                               float scale, int causal, void* stream) {
+  attn_status st = check_common(B, H, N, d, dtype, scale);
+  if (st != ATTN_OK) return st;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o) || !tensor_ok(dO) || !tensor_ok(dq) ||
+      !tensor_ok(dk) || !tensor_ok(dv))
+    return ATTN_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
+  if (!(dtype == ATTN_BF16 && (d == 64 || d == 128))) return ATTN_ERR_UNSUPPORTED;
+  if (workspace == nullptr || !aligned(workspace, 16)) return ATTN_ERR_WORKSPACE;
+  if (workspace_bytes < attn_bwd_atomic_workspace_bytes(B, H, N, d)) return ATTN_ERR_WORKSPACE;
+  attn::BwdArgs a{q, k, v, o, dO, lse, dq, dk, dv, static_cast<float*>(workspace), B, H, N, d, scale, causal != 0};
+  a.dqacc = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + bwd_terms_bytes_aligned(B, H, N));
+  return from_hip(attn::launch_bwd_atomic_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -15,6 +15,16 @@
 //                    S^T = K Q^T, dP^T = V dO^T, dS^T = P^T o (dP^T - D),
 //                    dQ^T += K^T dS^T.
 // dK and dQ are multiplied by the softmax scale at the end (section 8.8.4).
+//
+// Variant with atomic dQ (the single-pass alternative that section 8.8
+// contrasts with the split into a dK/dV and a dQ kernel): bwd_dkdv also adds
+// every tile's dS K into an fp32 dQ accumulator with atomic adds, and a
+// final pass scales it into dQ.  The workgroup puts its dS tile in LDS as
+// [key][query] and its K rows as [key][dim]; both go through the same
+// transposing reads, so dQ = dS K contracts over the workgroup's 128 keys in
+// one 32 x 32 output block per wavefront (two for d = 128), one atomic per
+// element and workgroup.  The summation order then depends on timing, so
+// this variant is not bitwise deterministic.
 // Tiles go HBM -> LDS with direct-to-LDS copies into the swizzled tile layout
 // of common.h, in a ring of buffers copied ahead of use.  Products that
 // contract over the sequence take their P / dS operand straight from the
@@ -117,13 +127,14 @@ __global__ __launch_bounds__(kThreads) void bwd_preprocess_kernel(const __bf16* 
 // ---------------------------------------------------------------------------
 // dK, dV: key tiles outer.  LDS buffer: Q tile | dO tile | nl2[64] | dsplit[64].
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL>
+template <int D, bool CAUSAL, bool ATOMIC_DQ = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 2 : 1))) void bwd_dkdv_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     const __bf16* __restrict__ dO, const float* __restrict__ nl2, const u32x2* __restrict__ dsplit,
-    __bf16* __restrict__ dK, __bf16* __restrict__ dV, int N, int BH, int n_ktiles, int group, float scale,
-    float scale_log2) {
+    __bf16* __restrict__ dK, __bf16* __restrict__ dV, float* __restrict__ dqacc, int N, int BH, int n_ktiles,
+    int group, float scale, float scale_log2) {
   using T = TileLayout<D>;
+  using TX = TileLayout<64>;  // dS tile of the atomic-dQ variant: [128 keys][64 queries]
   constexpr int BK = kWaves * 32;
   constexpr int NB = D == 64 ? 4 : 2;  // ring depth; tiles are copied NB/2 ahead
   constexpr int kBuf = 2 * T::kBytes + kT * 4 + kT * 8;
@@ -131,6 +142,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
   __shared__ __attribute__((aligned(1024))) unsigned char sb1[kBuf];
   __shared__ __attribute__((aligned(1024))) unsigned char sb2[NB > 2 ? kBuf : 16];
   __shared__ __attribute__((aligned(1024))) unsigned char sb3[NB > 2 ? kBuf : 16];
+  // atomic-dQ variant: the workgroup's K rows and the dS of two tiles (the
+  // dS of tile s is contracted at step s + 1, while tile s + 1 fills the
+  // other buffer)
+  __shared__ __attribute__((aligned(1024))) unsigned char skt[ATOMIC_DQ ? 2 * T::kBytes : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char sx0[ATOMIC_DQ ? 2 * TX::kBytes : 16];
+  __shared__ __attribute__((aligned(1024))) unsigned char sx1[ATOMIC_DQ ? 2 * TX::kBytes : 16];
 
   int bh, ktile;  // key tile 0 has the most query tiles under causal masking
   head_tile(xcd_remap(blockIdx.x, BH * n_ktiles), n_ktiles, BH, group, bh, ktile);
@@ -168,6 +185,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
   const int i_end = (N + kT - 1) / kT;
   const int ntiles = i_end - i_begin;
   constexpr int A = NB / 2;
+  // the K rows first: they are older than every tile copy, so the first
+  // tile's wait covers them
+  if constexpr (ATOMIC_DQ) {
+    cp.issue(K + base, k0, N, skt);
+    cp.issue(K + base, k0 + kT, N, skt + T::kBytes);
+  }
 #pragma unroll
   for (int p = 0; p < A; ++p)
     if (p < ntiles) issue_tile(i_begin + p, p == 0 ? sb0 : sb1);
@@ -185,14 +208,25 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) dk[mt] = dv[mt] = f32x16{};
 
-  auto compute = [&](int it, const unsigned char* buf) __attribute__((always_inline)) {
+  // atomic-dQ variant: this lane's row of a dS tile (key kw0 + l32)
+  const int xr = wave * 32 + l32;
+  const int xrow = (xr >> 6) * TX::kBytes;
+  auto compute = [&](int it, const unsigned char* buf, unsigned char* xt) __attribute__((always_inline)) {
+    unsigned char* const xrp = xt + xrow;
     const int q0 = it * kT;
-    if (CAUSAL && q0 + kT - 1 < kw0) return;  // every query of the tile is above this wavefront's keys
+    if (CAUSAL && q0 + kT - 1 < kw0) {  // every query of the tile is above this wavefront's keys
+      if constexpr (ATOMIC_DQ) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) *reinterpret_cast<u32x4*>(xrp + TX::offset(xr & 63, c)) = u32x4{};
+      }
+      return;
+    }
     const unsigned char* Qt = buf;
     const unsigned char* Dt = buf + T::kBytes;
     const float* ls = reinterpret_cast<const float*>(buf + 2 * T::kBytes);
     const u32x2* dsl = reinterpret_cast<const u32x2*>(buf + 2 * T::kBytes + kT * 4);
-    const bool need_mask = (q0 + kT > N) || (CAUSAL && q0 < kw0 + 31);
+    // keys past N only matter where dS leaves the workgroup (atomic dQ)
+    const bool need_mask = (q0 + kT > N) || (CAUSAL && q0 < kw0 + 31) || (ATOMIC_DQ && kw0 + 32 > N);
     // the two 32-query halves one after the other, so that only one pair of
     // score accumulators is live
 #pragma unroll
@@ -214,7 +248,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int qi = q0 + 32 * qh + acc_row(i, g);
-          if (qi >= N || (CAUSAL && key > qi)) sacc[i] = kNegInf;
+          if (qi >= N || (CAUSAL && key > qi) || (ATOMIC_DQ && key >= N)) sacc[i] = kNegInf;
         }
       }
       // P = exp2(S*c - LSE*log2e), dS = P o (dP - D)
@@ -244,6 +278,38 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
           dv[mt] = mfma32x32x16(of.tr(Dt, 2 * qh + tt, mt), pb, dv[mt]);
           dk[mt] = mfma32x32x16(of.tr(Qt, 2 * qh + tt, mt), sbf, dk[mt]);
         }
+        if constexpr (ATOMIC_DQ) {
+          // dS of queries 32qh + 16tt + 4g + 0..3 and +8 (the accumulator's
+          // row order) into the lane's row of the dS tile
+          const u32x4 w = bitcast<u32x4>(sbf);
+          *reinterpret_cast<u32x2*>(xrp + TX::offset(xr & 63, 4 * qh + 2 * tt) + 8 * g) = u32x2{w[0], w[1]};
+          *reinterpret_cast<u32x2*>(xrp + TX::offset(xr & 63, 4 * qh + 2 * tt + 1) + 8 * g) = u32x2{w[2], w[3]};
+        }
+      }
+    }
+  };
+
+  // atomic-dQ variant: dQ[q0 .. q0+63] += dS K over the workgroup's keys.
+  // Wavefront w owns query rows 32(w & 1) .. +31 and dims 32(w >> 1) .. +31
+  // (and +64 for d = 128); both operands are transposing reads in the same
+  // key order, the result lands with one fp32 atomic add per element.
+  const TileOffsets<64> ox(lane);
+  auto dq_tile = [&](int it, const unsigned char* xt) __attribute__((always_inline)) {
+    const int q0 = it * kT;
+    const int qb = 32 * (wave & 1);
+#pragma unroll
+    for (int nb = 0; nb < D / 64; ++nb) {
+      const int mtk = (wave >> 1) + 2 * nb;
+      f32x16 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < BK / 16; ++kk)
+        acc = mfma32x32x16(ox.tr(xt + (kk >> 2) * TX::kBytes, kk & 3, qb >> 5),
+                           of.tr(skt + (kk >> 2) * T::kBytes, kk & 3, mtk), acc);
+      float* dst = dqacc + ((int64_t)bh * N + q0 + qb) * D + 32 * mtk + l32;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int r = acc_row(i, g);
+        if (q0 + qb + r < N) atomicAdd(dst + (int64_t)r * D, acc[i]);
       }
     }
   };
@@ -251,7 +317,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
   // Tile s of the sweep (query tile i_begin + s) is in buffer s % NB; at its
   // step the copies of tile s + A go to buffer (s + A) % NB, which held tile
   // s - A (NB = 2A) and is free after the barrier.
-  auto step = [&](int s, const unsigned char* buf, unsigned char* next) __attribute__((always_inline)) {
+  // (Atomic dQ: the dS of tile s - 1, complete since the barrier, is
+  // contracted and added before tile s is computed, so the adds are in flight
+  // during that work.  The copy waits below count only tile copies: a wait
+  // for tile s cannot pass before it lands, since loads complete in order and
+  // the adds only raise the count.)
+  auto step = [&](int s, const unsigned char* buf, unsigned char* next, unsigned char* xcur,
+                  const unsigned char* xprev) __attribute__((always_inline)) {
     if (s + A - 1 < ntiles) {
       if (wave < 3) wait_vm_at_most<(A - 1) * (kCopies + 1)>(); else wait_vm_at_most<(A - 1) * kCopies>();
     } else {
@@ -259,21 +331,31 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 6
     }
     lds_barrier();
     if (s + A < ntiles) issue_tile(i_begin + s + A, next);
-    if (s < ntiles) compute(i_begin + s, buf);
+    if constexpr (ATOMIC_DQ) {
+      if (s >= 1 && s - 1 < ntiles) dq_tile(i_begin + s - 1, xprev);
+    }
+    if (s < ntiles) compute(i_begin + s, buf, xcur);
   };
   // one exit per loop (steps past the end only wait and synchronise), so the
   // accumulators keep their registers across iterations
   if constexpr (NB == 4) {
     for (int s = 0; s < ntiles; s += 4) {
-      step(s, sb0, sb2);
-      step(s + 1, sb1, sb3);
-      step(s + 2, sb2, sb0);
-      step(s + 3, sb3, sb1);
+      step(s, sb0, sb2, sx0, sx1);
+      step(s + 1, sb1, sb3, sx1, sx0);
+      step(s + 2, sb2, sb0, sx0, sx1);
+      step(s + 3, sb3, sb1, sx1, sx0);
     }
   } else {
     for (int s = 0; s < ntiles; s += 2) {
-      step(s, sb0, sb1);
-      step(s + 1, sb1, sb0);
+      step(s, sb0, sb1, sx0, sx1);
+      step(s + 1, sb1, sb0, sx1, sx0);
+    }
+  }
+  if constexpr (ATOMIC_DQ) {
+    // the last tile's dS when the loop ended on it (its index is odd)
+    if (ntiles % NB == 0) {
+      lds_barrier();
+      dq_tile(i_begin + ntiles - 1, sx1);
     }
   }
 
@@ -812,21 +894,58 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   if (qr < N) store_transposed_acc<D>(dQ + base + (int64_t)qr * D, dq, g, scale);
 }
 
-template <int D, bool CAUSAL>
-hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
-  const int BH = a.B * a.H;
-  const int64_t rows = (int64_t)BH * a.N;
-  // workspace: delta [rows] f32 | nl2 [rows] f32 | dsplit [rows] x 8 bytes | lsplit [rows] x 8 bytes
-  const float scale_log2 = a.scale * kLog2e;
-  float* nl2 = a.delta + rows;
-  u32x2* dsplit = reinterpret_cast<u32x2*>(a.delta + 2 * rows);
-  u32x2* lsplit = dsplit + rows;
+// fp32 zero fill (the atomic dQ accumulator; a kernel rather than a memset,
+// so that the sequence can be captured in a graph)
+__global__ __launch_bounds__(kThreads) void zero_f32x4_kernel(f32x4* __restrict__ p, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kThreads)
+    p[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+// dQ = scale * accumulator, rounded to bf16 (RNE)
+__global__ __launch_bounds__(kThreads) void dq_convert_kernel(const f32x4* __restrict__ acc, u32x2* __restrict__ dq,
+                                                              float scale, int64_t n4) {
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n4; i += (int64_t)gridDim.x * kThreads) {
+    const f32x4 v = acc[i];
+    dq[i] = u32x2{pack_bf16x2(v[0] * scale, v[1] * scale), pack_bf16x2(v[2] * scale, v[3] * scale)};
+  }
+}
+
+unsigned stream_grid(int64_t n4) {
+  const int64_t wg = (n4 + kThreads - 1) / kThreads;
+  return (unsigned)(wg < 16384 ? (wg > 0 ? wg : 1) : 16384);
+}
+
+// Per-row terms in the workspace: delta [rows] f32 | nl2 [rows] f32 |
+// dsplit [rows] x 8 bytes | lsplit [rows] x 8 bytes
+struct RowTerms {
+  float* nl2;
+  u32x2* dsplit;
+  u32x2* lsplit;
+};
+
+template <int D>
+hipError_t run_preprocess(const BwdArgs& a, hipStream_t s, RowTerms& t) {
+  const int64_t rows = (int64_t)a.B * a.H * a.N;
+  t.nl2 = a.delta + rows;
+  t.dsplit = reinterpret_cast<u32x2*>(a.delta + 2 * rows);
+  t.lsplit = t.dsplit + rows;
   constexpr int rows_per_wg = kThreads / (D / 8);
   hipLaunchKernelGGL((bwd_preprocess_kernel<D>), dim3((unsigned)((rows + rows_per_wg - 1) / rows_per_wg)),
                      dim3(kThreads), 0, s, static_cast<const __bf16*>(a.o), static_cast<const __bf16*>(a.dO),
-                     a.lse, a.delta, nl2, dsplit, lsplit, scale_log2, rows);
-  hipError_t e = hipGetLastError();
+                     a.lse, a.delta, t.nl2, t.dsplit, t.lsplit, a.scale * kLog2e, rows);
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL>
+hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
+  const int BH = a.B * a.H;
+  const float scale_log2 = a.scale * kLog2e;
+  RowTerms rt;
+  hipError_t e = run_preprocess<D>(a, s, rt);
   if (e != hipSuccess) return e;
+  float* nl2 = rt.nl2;
+  u32x2* dsplit = rt.dsplit;
+  u32x2* lsplit = rt.lsplit;
 
   const int group = BH >= kNumXcd ? BH / kNumXcd : 1;
   if constexpr (D == 64) {
@@ -849,8 +968,8 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_kt * BH), dim3(kThreads), 0, s,
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                      static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), nl2, dsplit,
-                     static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.N, BH, n_kt, group, a.scale,
-                     scale_log2);
+                     static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), nullptr, a.N, BH, n_kt, group,
+                     a.scale, scale_log2);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
 
@@ -862,7 +981,39 @@ hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The atomic-dQ variant: preprocess, zero the fp32 accumulator, dK/dV with
+// the dQ atomics, scale the accumulator into dQ.
+template <int D, bool CAUSAL>
+hipError_t run_bwd_atomic(const BwdArgs& a, hipStream_t s) {
+  const int BH = a.B * a.H;
+  const int64_t n4 = (int64_t)BH * a.N * D / 4;
+  RowTerms rt;
+  hipError_t e = run_preprocess<D>(a, s, rt);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(zero_f32x4_kernel, dim3(stream_grid(n4)), dim3(kThreads), 0, s,
+                     reinterpret_cast<f32x4*>(a.dqacc), n4);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int group = BH >= kNumXcd ? BH / kNumXcd : 1;
+  const int n_kt = (a.N + kWaves * 32 - 1) / (kWaves * 32);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL, true>), dim3(n_kt * BH), dim3(kThreads), 0, s,
+                     static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                     static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), rt.nl2, rt.dsplit,
+                     static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.dqacc, a.N, BH, n_kt, group,
+                     a.scale, a.scale * kLog2e);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(dq_convert_kernel, dim3(stream_grid(n4)), dim3(kThreads), 0, s,
+                     reinterpret_cast<const f32x4*>(a.dqacc), static_cast<u32x2*>(a.dq), a.scale, n4);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_bwd_atomic_bf16(const BwdArgs& a, hipStream_t s) {
+  if (a.d == 64) return a.causal ? run_bwd_atomic<64, true>(a, s) : run_bwd_atomic<64, false>(a, s);
+  return a.causal ? run_bwd_atomic<128, true>(a, s) : run_bwd_atomic<128, false>(a, s);
+}
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s) {
   if (a.d == 64) return a.causal ? run_bwd<64, true>(a, s) : run_bwd<64, false>(a, s);

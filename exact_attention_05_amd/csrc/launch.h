@@ -105,8 +105,10 @@ struct BwdArgs {
   int B, H, N, d;
   float scale;
   int causal;
+  float* dqacc = nullptr;  // atomic-dQ variant: fp32 dQ accumulator [B*H*N*d]
 };
 
 hipError_t launch_bwd_bf16(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_atomic_bf16(const BwdArgs& a, hipStream_t s);
 
 }  // namespace attn

@@ -13,6 +13,7 @@
  *                           the same decode over a paged cache addressed
  *                           through a per-sequence block table.
  *   attn_bwd                dQ, dK, dV by recomputing P from the saved LSE.
+ *   attn_bwd_atomic_dq      the same with dQ accumulated by atomic adds.
  *   attn_quantize_fp8, attn_fwd_fp8
  *                           FP8 (E4M3) storage with per-block scales, and
  *                           the forward on it.
@@ -295,6 +296,35 @@ attn_status attn_bwd(const void* q, const void* k, const void* v, const void* o,
                      const float* lse, void* dq, void* dk, void* dv, void* workspace,
                      size_t workspace_bytes, int B, int H, int N, int d, attn_dtype dtype,
                      float scale, int causal, void* stream);
+
+/*
+ * Workspace size in bytes that attn_bwd_atomic_dq needs: the 24 bytes per
+ * query row of attn_bwd_workspace_bytes, rounded up to 256 bytes, then an
+ * fp32 dQ accumulator of B*H*N*d values.  Returns 0 for invalid sizes.
+ */
+size_t attn_bwd_atomic_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * attn_bwd_atomic_dq -- the same backward with dQ accumulated by atomic adds
+ * in the dK/dV pass (the single-kernel alternative to the split into a dK/dV
+ * and a dQ pass, "8. FlashAttention 实战", triton-tutorial.pages.dev,
+ * section 8.8.4): every key tile adds its dS K into an fp32 accumulator in
+ * the workspace, which a last pass multiplies by scale into dq.  The results
+ * are those of attn_bwd up to the order of the fp32 additions into dQ; that
+ * order depends on timing, so dq is not bitwise reproducible (dk and dv are).
+ *
+ *   q, k, v, o, dO, lse, dq, dk, dv : as attn_bwd
+ *   workspace      : >= attn_bwd_atomic_workspace_bytes(B, H, N, d) bytes,
+ *                    16-byte aligned; its first B*H*N fp32 values hold D on
+ *                    return, the accumulator holds dQ / scale.
+ *
+ * Supported: ATTN_BF16 with d in {64, 128}.
+ * Errors as attn_bwd.
+ */
+attn_status attn_bwd_atomic_dq(const void* q, const void* k, const void* v, const void* o, const void* dO,
+                               const float* lse, void* dq, void* dk, void* dv, void* workspace,
+                               size_t workspace_bytes, int B, int H, int N, int d, attn_dtype dtype,
+                               float scale, int causal, void* stream);
 
 #ifdef __cplusplus
 }

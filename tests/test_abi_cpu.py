@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     for n in ("attn_fwd", "attn_fwd_splitk_decode", "attn_fwd_splitk_decode_paged", "attn_bwd",
               "attn_quantize_fp8", "attn_fwd_fp8", "attn_merge",
               "attn_decode_workspace_bytes",
-              "attn_bwd_workspace_bytes", "attn_status_string", "attn_abi_version"):
+              "attn_bwd_workspace_bytes", "attn_bwd_atomic_dq", "attn_bwd_atomic_workspace_bytes",
+              "attn_status_string", "attn_abi_version"):
         assert n in names
 
 
@@ -65,6 +66,10 @@ def test_workspace_sizes():
     assert lib.attn_decode_workspace_bytes(1, 1, 64, 0) == 0
     assert lib.attn_bwd_workspace_bytes(2, 16, 4096) == 2 * 16 * 4096 * 24
     assert lib.attn_bwd_workspace_bytes(1, 1, 0) == 0
+    # the per-row terms rounded up to 256 bytes, then the fp32 dQ accumulator
+    assert lib.attn_bwd_atomic_workspace_bytes(2, 16, 4096, 64) == 2 * 16 * 4096 * (24 + 64 * 4)
+    assert lib.attn_bwd_atomic_workspace_bytes(1, 1, 3, 64) == 256 + 3 * 64 * 4
+    assert lib.attn_bwd_atomic_workspace_bytes(1, 1, 0, 64) == 0
 
 
 @pytest.mark.parametrize(
@@ -220,10 +225,12 @@ def test_merge_validation():
     assert call(d=32, dt=F32) == UNSUPPORTED
 
 
-def test_bwd_validation():
+@pytest.mark.parametrize("entry", ["attn_bwd", "attn_bwd_atomic_dq"])
+def test_bwd_validation(entry):
     lib = _lib()
-    f = lib.attn_bwd
-    need = lib.attn_bwd_workspace_bytes(1, 2, 64)
+    f = getattr(lib, entry)
+    need = (lib.attn_bwd_workspace_bytes(1, 2, 64) if entry == "attn_bwd"
+            else lib.attn_bwd_atomic_workspace_bytes(1, 2, 64, 64))
     base = dict(q=P, k=P, v=P, o=P, do=P, lse=P, dq=P, dk=P, dv=P, ws=P, wsb=need, B=1, H=2, N=64, d=64,
                 dt=BF16, sc=0.125, causal=1)
 
