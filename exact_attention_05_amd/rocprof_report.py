@@ -138,7 +138,7 @@ def cmd_stats(a):
             grid = int(g)
         amt, unit = rest.split(":")
         work.append((rx, grid, float(amt), unit))
-    lines = [f"# {a.title}", "", "Command (GPU box, repo root):", "", "```", a.cmd, "```", ""]
+    lines = [f"# {a.title}", "", "Command (MI355X host, repository root):", "", "```", a.cmd, "```", ""]
     lines.append("| kernel | grid (work-items) | calls | average (us) | min (us) | max (us) | share | achieved vs peak |")
     lines.append("|---|---|---|---|---|---|---|---|")
     for name, grid, calls, avg, mn, mx, pct in rows:
@@ -197,7 +197,7 @@ def cmd_traffic(a):
         json.dump(tab, f, indent=1, sort_keys=True)
         f.write("\n")
     lines = [
-        f"# HBM traffic of `{a.kernel}` ({a.key})", "", "Commands (GPU box, repo root):", "", "```", a.cmd, "```", "",
+        f"# HBM traffic of `{a.kernel}` ({a.key})", "", "Commands (MI355X host, repository root):", "", "```", a.cmd, "```", "",
         f"Calibration: a device copy of {a.calib_mib} MiB reads FETCH_SIZE = {f_copy:.1f} KiB and "
         f"WRITE_SIZE = {w_copy:.1f} KiB, so the counters are scaled by {f_scale:.4f} (fetch) and "
         f"{w_scale:.4f} (write).", "",
