@@ -13,7 +13,8 @@ inputs:
   * one GPU's share of an 8-GPU Ring Attention over the long causal
     forward's inputs (the last GPU: its causal diagonal shard, then seven
     earlier 1024-token K/V shards, each forward merged into its running
-    result; reported only)
+    result; reported only), and the same steps replayed as one captured HIP
+    graph (reported only)
   * forward on FP8 (E4M3) storage of the headline Q, K, V (per-block
     power-of-two scales: Q per 128 rows, K and V per 64; quantised before the
     timed region), non-causal (reported only)
@@ -204,16 +205,17 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--only", default="",
-                    help="comma-separated subset of fwd,decode,bwd,fwd_long,decode_paged,fwd_fp8,ring,bwd_atomic "
+                    help="comma-separated subset of fwd,decode,bwd,fwd_long,decode_paged,fwd_fp8,ring,ring_graph,"
+                         "bwd_atomic "
                          "to run "
                          "(profiling passes)")
     a = ap.parse_args()
-    parts = (["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long", "ring"])
+    parts = (["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long", "ring", "ring_graph"])
              + ["decode_paged", "fwd_fp8", "bwd_atomic"])
     if a.only:
         parts = [p for p in a.only.split(",") if p]
         bad = [p for p in parts if p not in ("fwd", "decode", "bwd", "fwd_long", "decode_paged", "fwd_fp8", "ring",
-                                             "bwd_atomic")]
+                                             "ring_graph", "bwd_atomic")]
         if bad:
             ap.error(f"unknown --only parts {bad}")
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -291,12 +293,12 @@ def main():
         c = BWD
         aws = torch.empty(attn_bwd_atomic_workspace_bytes(c["B"], c["H"], c["N"], c["d"]) // 4,
                           dtype=torch.float32, device=dev)
-    if "fwd_long" in parts or "ring" in parts:
+    if "fwd_long" in parts or "ring" in parts or "ring_graph" in parts:
         c = FWD_LONG
         lq, lk, lv = mk(0, ("q", "k", "v"), c["B"], c["H"], c["N"], c["d"], c["input_scale"])
         lo = torch.empty_like(lq)
         llse = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device=dev)
-    if "ring" in parts:
+    if "ring" in parts or "ring_graph" in parts:
         S = FWD_LONG["N"] // RING_G
         sh = lambda t, j: t[:, :, j * S:(j + 1) * S].contiguous()
         me = RING_G - 1  # the last GPU: the most shards below its diagonal
@@ -305,6 +307,25 @@ def main():
         rv = [sh(lv, j) for j in range(RING_G)]
         ro, rl = torch.empty_like(rq), torch.empty(rq.shape[:3], dtype=torch.float32, device=dev)
         rpo, rpl = torch.empty_like(rq), torch.empty_like(rl)
+
+    def ring_share(o, l, po, pl):
+        attn_fwd(rq, rk[me], rv[me], causal=True, out=o, lse=l)
+        for j in range(me - 1, -1, -1):
+            attn_fwd(rq, rk[j], rv[j], causal=False, out=po, lse=pl)
+            attn_merge(o, l, po, pl, out=o, lse=l)
+
+    if "ring_graph" in parts:
+        # the ring share's 15 launches captured once, replayed per step
+        go, gl, gpo, gpl = (torch.empty_like(t) for t in (ro, rl, rpo, rpl))
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            ring_share(go, gl, gpo, gpl)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        torch.cuda.synchronize()
+        ring_g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ring_g):
+            ring_share(go, gl, gpo, gpl)
     torch.cuda.synchronize()
     print("bench: inputs resident", file=sys.stderr, flush=True)
 
@@ -337,11 +358,12 @@ def main():
             ev["fwd_long"][1].record(stream)
         if "ring" in names:
             ev["ring"][0].record(stream)
-            attn_fwd(rq, rk[me], rv[me], causal=True, out=ro, lse=rl)
-            for j in range(me - 1, -1, -1):
-                attn_fwd(rq, rk[j], rv[j], causal=False, out=rpo, lse=rpl)
-                attn_merge(ro, rl, rpo, rpl, out=ro, lse=rl)
+            ring_share(ro, rl, rpo, rpl)
             ev["ring"][1].record(stream)
+        if "ring_graph" in names:
+            ev["ring_graph"][0].record(stream)
+            ring_g.replay()
+            ev["ring_graph"][1].record(stream)
         if "fwd_fp8" in names:
             ev["fwd_fp8"][0].record(stream)
             attn_fwd_fp8(q8, k8, v8, sq8, sk8, sv8, FP8_BLOCKS[0], FP8_BLOCKS[1], causal=False, out=o8, lse=lse8)
@@ -403,7 +425,8 @@ def main():
                         "bf16 q[16,32,1,128] x KV[16,32,32768,128], 256 chunks; backward bf16 [2,16,4096,64] "
                         "causal; forward bf16 [2,32,8192,128] causal (reported); the same decode over a "
                         "paged cache of 16-token blocks (reported); the headline forward on FP8 E4M3 storage "
-                        "(reported); one GPU's share of an 8-GPU ring over the long causal forward (reported); "
+                        "(reported); one GPU's share of an 8-GPU ring over the long causal forward, eager and as a "
+                        "replayed HIP graph (reported); "
                         "the backward with atomic dQ (reported)",
             "global_batch": FWD["B"],
             "seq_len": FWD["N"],
@@ -464,6 +487,14 @@ def main():
         ring_flops = 4.0 * c["B"] * c["H"] * S * S * c["d"] * ((RING_G - 1) + 0.5)
         out["ring_share_tflops"] = round(ring_flops / (ms["ring"] * 1e-3) / 1e12, 3)
         out["ring_share_us"] = round(ms["ring"] * 1e3, 2)
+    if "ring_graph" in ms:
+        c = FWD_LONG
+        S = c["N"] // RING_G
+        ring_flops = 4.0 * c["B"] * c["H"] * S * S * c["d"] * ((RING_G - 1) + 0.5)
+        out["ring_share_graph_tflops"] = round(ring_flops / (ms["ring_graph"] * 1e-3) / 1e12, 3)
+        out["ring_share_graph_us"] = round(ms["ring_graph"] * 1e3, 2)
+        if "ring" in ms:
+            out["ring_graph_equals_eager"] = bool(torch.equal(go, ro) and torch.equal(gl, rl))
     if "fwd_fp8" in ms:
         f8 = rate("fwd_fp8", fwd_flops(FWD), 1e12)
         out["fwd_fp8_tflops"] = round(f8, 3)
