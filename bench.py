@@ -13,8 +13,9 @@ inputs:
   * one GPU's share of an 8-GPU Ring Attention over the long causal
     forward's inputs (the last GPU: its causal diagonal shard, then seven
     earlier 1024-token K/V shards, each forward merged into its running
-    result; reported only), and the same steps replayed as one captured HIP
-    graph (reported only)
+    result in its epilogue; reported only), the same with a separate merge
+    kernel per shard, and the fused steps replayed as one captured HIP graph
+    (reported only)
   * forward on FP8 (E4M3) storage of the headline Q, K, V (per-block
     power-of-two scales: Q per 128 rows, K and V per 64; quantised before the
     timed region), non-causal (reported only)
@@ -205,17 +206,18 @@ def main():
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--only", default="",
-                    help="comma-separated subset of fwd,decode,bwd,fwd_long,decode_paged,fwd_fp8,ring,ring_graph,"
+                    help="comma-separated subset of fwd,decode,bwd,fwd_long,decode_paged,fwd_fp8,ring,ring_unfused,"
+                         "ring_graph,"
                          "bwd_atomic "
                          "to run "
                          "(profiling passes)")
     a = ap.parse_args()
-    parts = (["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long", "ring", "ring_graph"])
+    parts = (["fwd", "decode", "bwd"] + ([] if a.no_long else ["fwd_long", "ring", "ring_unfused", "ring_graph"])
              + ["decode_paged", "fwd_fp8", "bwd_atomic"])
     if a.only:
         parts = [p for p in a.only.split(",") if p]
         bad = [p for p in parts if p not in ("fwd", "decode", "bwd", "fwd_long", "decode_paged", "fwd_fp8", "ring",
-                                             "ring_graph", "bwd_atomic")]
+                                             "ring_unfused", "ring_graph", "bwd_atomic")]
         if bad:
             ap.error(f"unknown --only parts {bad}")
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -225,8 +227,9 @@ def main():
 
     import torch
 
-    from exact_attention_05_amd import (attn_bwd, attn_bwd_atomic_dq, attn_fwd, attn_fwd_fp8, attn_fwd_splitk_decode,
-                                        attn_fwd_splitk_decode_paged, attn_merge, attn_quantize_fp8)
+    from exact_attention_05_amd import (attn_bwd, attn_bwd_atomic_dq, attn_fwd, attn_fwd_fp8, attn_fwd_merge,
+                                        attn_fwd_splitk_decode, attn_fwd_splitk_decode_paged, attn_merge,
+                                        attn_quantize_fp8)
     from exact_attention_05_amd.binding import (attn_bwd_atomic_workspace_bytes, attn_bwd_workspace_bytes,
                                                 attn_decode_workspace_bytes)
     from exact_attention_05_amd.inputs import make_block_table, make_tensor
@@ -293,12 +296,12 @@ def main():
         c = BWD
         aws = torch.empty(attn_bwd_atomic_workspace_bytes(c["B"], c["H"], c["N"], c["d"]) // 4,
                           dtype=torch.float32, device=dev)
-    if "fwd_long" in parts or "ring" in parts or "ring_graph" in parts:
+    if "fwd_long" in parts or any(p.startswith("ring") for p in parts):
         c = FWD_LONG
         lq, lk, lv = mk(0, ("q", "k", "v"), c["B"], c["H"], c["N"], c["d"], c["input_scale"])
         lo = torch.empty_like(lq)
         llse = torch.empty((c["B"], c["H"], c["N"]), dtype=torch.float32, device=dev)
-    if "ring" in parts or "ring_graph" in parts:
+    if any(p.startswith("ring") for p in parts):
         S = FWD_LONG["N"] // RING_G
         sh = lambda t, j: t[:, :, j * S:(j + 1) * S].contiguous()
         me = RING_G - 1  # the last GPU: the most shards below its diagonal
@@ -307,12 +310,16 @@ def main():
         rv = [sh(lv, j) for j in range(RING_G)]
         ro, rl = torch.empty_like(rq), torch.empty(rq.shape[:3], dtype=torch.float32, device=dev)
         rpo, rpl = torch.empty_like(rq), torch.empty_like(rl)
+        uo, ul = torch.empty_like(rq), torch.empty_like(rl)
 
-    def ring_share(o, l, po, pl):
+    def ring_share(o, l, po, pl, fused=True):
         attn_fwd(rq, rk[me], rv[me], causal=True, out=o, lse=l)
         for j in range(me - 1, -1, -1):
-            attn_fwd(rq, rk[j], rv[j], causal=False, out=po, lse=pl)
-            attn_merge(o, l, po, pl, out=o, lse=l)
+            if fused:
+                attn_fwd_merge(rq, rk[j], rv[j], o, l)
+            else:
+                attn_fwd(rq, rk[j], rv[j], causal=False, out=po, lse=pl)
+                attn_merge(o, l, po, pl, out=o, lse=l)
 
     if "ring_graph" in parts:
         # the ring share's 15 launches captured once, replayed per step
@@ -360,6 +367,10 @@ def main():
             ev["ring"][0].record(stream)
             ring_share(ro, rl, rpo, rpl)
             ev["ring"][1].record(stream)
+        if "ring_unfused" in names:
+            ev["ring_unfused"][0].record(stream)
+            ring_share(uo, ul, rpo, rpl, fused=False)
+            ev["ring_unfused"][1].record(stream)
         if "ring_graph" in names:
             ev["ring_graph"][0].record(stream)
             ring_g.replay()
@@ -425,8 +436,8 @@ def main():
                         "bf16 q[16,32,1,128] x KV[16,32,32768,128], 256 chunks; backward bf16 [2,16,4096,64] "
                         "causal; forward bf16 [2,32,8192,128] causal (reported); the same decode over a "
                         "paged cache of 16-token blocks (reported); the headline forward on FP8 E4M3 storage "
-                        "(reported); one GPU's share of an 8-GPU ring over the long causal forward, eager and as a "
-                        "replayed HIP graph (reported); "
+                        "(reported); one GPU's share of an 8-GPU ring over the long causal forward: merge fused, "
+                        "separate and as a replayed HIP graph (reported); "
                         "the backward with atomic dQ (reported)",
             "global_batch": FWD["B"],
             "seq_len": FWD["N"],
@@ -495,6 +506,12 @@ def main():
         out["ring_share_graph_us"] = round(ms["ring_graph"] * 1e3, 2)
         if "ring" in ms:
             out["ring_graph_equals_eager"] = bool(torch.equal(go, ro) and torch.equal(gl, rl))
+    if "ring_unfused" in ms:
+        c = FWD_LONG
+        S = c["N"] // RING_G
+        ring_flops = 4.0 * c["B"] * c["H"] * S * S * c["d"] * ((RING_G - 1) + 0.5)
+        out["ring_share_unfused_tflops"] = round(ring_flops / (ms["ring_unfused"] * 1e-3) / 1e12, 3)
+        out["ring_share_unfused_us"] = round(ms["ring_unfused"] * 1e3, 2)
     if "fwd_fp8" in ms:
         f8 = rate("fwd_fp8", fwd_flops(FWD), 1e12)
         out["fwd_fp8_tflops"] = round(f8, 3)

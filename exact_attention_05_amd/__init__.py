@@ -8,6 +8,7 @@ first use, and every call fails loudly when it is missing.
 
 __all__ = [
     "attn_fwd",
+    "attn_fwd_merge",
     "attn_fwd_splitk_decode",
     "attn_fwd_splitk_decode_paged",
     "attn_bwd",

@@ -56,6 +56,8 @@ def _load():
     lib.attn_abi_version.argtypes = []
     lib.attn_fwd.restype = ci
     lib.attn_fwd.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.attn_fwd_merge.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, cf, ci, vp]
+    lib.attn_fwd_merge.restype = ci
     lib.attn_decode_workspace_bytes.restype = sz
     lib.attn_decode_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.attn_fwd_splitk_decode.restype = ci
@@ -143,6 +145,24 @@ def attn_fwd(q, k, v, scale=None, causal=False, out=None, lse=None):
                           scale, int(bool(causal)), _stream(dev))
     _check(st, "attn_fwd")
     return out, lse
+
+
+def attn_fwd_merge(q, k, v, o, lse, scale=None, causal=False):
+    """Attention of q over the keys k, v combined in place with the running
+    result (o, lse) over other keys (rows with lse = -inf have seen none).
+
+    Returns (o, lse), the same tensors, now over both key sets.
+    """
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o)):
+        _check_bhnd(name, t, (B, H, N, d), q.dtype, dev)
+    _check_bhnd("lse", lse, (B, H, N), torch.float32, dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    st = _load().attn_fwd_merge(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _dtype_code(q),
+                                scale, int(bool(causal)), _stream(dev))
+    _check(st, "attn_fwd_merge")
+    return o, lse
 
 
 def attn_decode_workspace_bytes(B, H, d, num_splits):

@@ -65,6 +65,18 @@ attn_status attn_fwd(const void* q, const void* k, const void* v, void* o, float
   return from_hip(dtype == ATTN_BF16 ? attn::launch_fwd_bf16(a, s) : attn::launch_fwd_f32(a, s));
 }
 
+attn_status attn_fwd_merge(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                           int d, attn_dtype dtype, float scale, int causal, void* stream) {
+  attn_status st = check_common(B, H, N, d, dtype, scale);
+  if (st != ATTN_OK) return st;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o)) return ATTN_ERR_INVALID_ARG;
+  if (lse == nullptr || !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
+  if (!(dtype == ATTN_BF16 && (d == 64 || d == 128))) return ATTN_ERR_UNSUPPORTED;
+  attn::FwdArgs a{q, k, v, o, lse, B, H, N, d, scale, causal != 0};
+  a.merge = true;
+  return from_hip(attn::launch_fwd_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t attn_decode_workspace_bytes(int B, int H, int d, int num_splits) {
   if (B < 1 || H < 1 || d < 1 || num_splits < 1) return 0;
   return (size_t)B * (size_t)H * (size_t)num_splits * ((size_t)d + 2) * sizeof(float);

@@ -51,7 +51,43 @@ constexpr int kBc = 64;  // keys per K/V tile
 // With partial sums below 2^64, U stays below 2^64 * N * max|v|.
 constexpr float kSumLimit = 18446744073709551616.f;  // 2^64
 
-template <int D, int QT, int NBUF, bool CAUSAL>
+// Fused merge (attn_fwd_merge): the result over the keys of earlier calls,
+// (O_prev, LSE_prev) in memory, and over this call's keys, (U / l, LSE_new),
+// combine into the result over both sets: with L = log(e^LSE_prev +
+// e^LSE_new), O = e^(LSE_prev - L) O_prev + e^(LSE_new - L) U / l ("Ring
+// Attention", the online-softmax update across key blocks).  Base 2 inside;
+// a side with LSE = -inf gets weight 0 and its O is not used.
+struct MergeWeights {
+  float wa, wb;  // weights of O_prev and of U / l, summing to 1 (both 0 if both sides are empty)
+  float lse;     // L
+};
+__device__ __forceinline__ MergeWeights merge_weights(float lse_prev, float lse2_new) {
+  const float a2 = lse_prev * kLog2e;
+  const float mx = fmaxf(a2, lse2_new);
+  if (mx == kNegInf) return {0.f, 0.f, kNegInf};
+  const float wa = fast_exp2(a2 - mx), wb = fast_exp2(lse2_new - mx);
+  const float tot = wa + wb;
+  const float r = 1.f / tot;
+  return {wa * r, wb * r, (mx + fast_log2(tot)) * kLn2};
+}
+// O of one lane's 4 consecutive dims: the new values x, merged with the bf16
+// values at dst when MERGE (dst is read before it is written, by this lane only)
+template <bool MERGE>
+__device__ __forceinline__ u32x2 merged_out4(const __bf16* dst, float x0, float x1, float x2, float x3,
+                                             const MergeWeights& w) {
+  if constexpr (MERGE) {
+    const u32x2 prev = *reinterpret_cast<const u32x2*>(dst);
+    float p[4] = {bf16lo_to_f32(prev[0]), bf16hi_to_f32(prev[0]), bf16lo_to_f32(prev[1]), bf16hi_to_f32(prev[1])};
+    const bool use_prev = w.wa > 0.f;
+    x0 = (use_prev ? w.wa * p[0] : 0.f) + w.wb * x0;
+    x1 = (use_prev ? w.wa * p[1] : 0.f) + w.wb * x1;
+    x2 = (use_prev ? w.wa * p[2] : 0.f) + w.wb * x2;
+    x3 = (use_prev ? w.wa * p[3] : 0.f) + w.wb * x3;
+  }
+  return u32x2{pack_bf16x2(x0, x1), pack_bf16x2(x2, x3)};
+}
+
+template <int D, int QT, int NBUF, bool CAUSAL, bool MERGE = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void fwd_bf16_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg,
@@ -332,25 +368,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   }
 
-  // Epilogue: O = U / l (bf16, RNE) and LSE = (m + log2 l) * ln 2.
+  // Epilogue: O = U / l (bf16, RNE) and LSE = (m + log2 l) * ln 2, or
+  // with MERGE both combined with the running result in O and LSE.
 #pragma unroll
   for (int nt = 0; nt < QT; ++nt) {
     const int qr = qw0 + nt * 32 + l32;
     const float lt = lsum[nt] + shfl_xor_f32(lsum[nt], 32);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    const float lse2 = lt > 0.f ? m2[nt] + fast_log2(lt) : kNegInf;
     if (qr < N) {
+      MergeWeights mw{0.f, 1.f, lse2 * kLn2};
+      if constexpr (MERGE) mw = merge_weights(LSE[(int64_t)bh * N + qr], lse2);
 #pragma unroll
       for (int mt = 0; mt < D / 32; ++mt) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const int d0 = 32 * mt + 8 * c + 4 * g;
-          u32x2 w = {pack_bf16x2(oacc[nt][mt][4 * c] * inv, oacc[nt][mt][4 * c + 1] * inv),
-                     pack_bf16x2(oacc[nt][mt][4 * c + 2] * inv, oacc[nt][mt][4 * c + 3] * inv)};
-          *reinterpret_cast<u32x2*>(Oh + (int64_t)qr * D + d0) = w;
+          __bf16* dst = Oh + (int64_t)qr * D + d0;
+          *reinterpret_cast<u32x2*>(dst) =
+              merged_out4<MERGE>(dst, oacc[nt][mt][4 * c] * inv, oacc[nt][mt][4 * c + 1] * inv,
+                                 oacc[nt][mt][4 * c + 2] * inv, oacc[nt][mt][4 * c + 3] * inv, mw);
         }
       }
-      if (g == 0 && LSE != nullptr)
-        LSE[(int64_t)bh * N + qr] = lt > 0.f ? (m2[nt] + fast_log2(lt)) * kLn2 : kNegInf;
+      if (g == 0 && LSE != nullptr) LSE[(int64_t)bh * N + qr] = mw.lse;
     }
   }
 }
@@ -524,7 +564,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
 // first reader of tile j+1.  Online state and reference rule as in
 // fwd_bf16_kernel.
 // ---------------------------------------------------------------------------
-template <bool CAUSAL>
+template <bool CAUSAL, bool MERGE = false>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void fwd_pp4_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg, float scale_log2) {
@@ -699,39 +739,42 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
 
   const float lt = lsum + shfl_xor_f32(lsum, 32);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const float lse2 = lt > 0.f ? m2 + fast_log2(lt) : kNegInf;
   if (qr < N) {
     __bf16* Oh = O + base;
+    MergeWeights mw{0.f, 1.f, lse2 * kLn2};
+    if constexpr (MERGE) mw = merge_weights(LSE[(int64_t)bh * N + qr], lse2);
 #pragma unroll
     for (int mt = 0; mt < D / 32; ++mt)
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int d0 = 32 * mt + 8 * c + 4 * g;
-        u32x2 w = {pack_bf16x2(oacc[mt][4 * c] * inv, oacc[mt][4 * c + 1] * inv),
-                   pack_bf16x2(oacc[mt][4 * c + 2] * inv, oacc[mt][4 * c + 3] * inv)};
-        *reinterpret_cast<u32x2*>(Oh + (int64_t)qr * D + d0) = w;
+        __bf16* dst = Oh + (int64_t)qr * D + d0;
+        *reinterpret_cast<u32x2*>(dst) = merged_out4<MERGE>(dst, oacc[mt][4 * c] * inv, oacc[mt][4 * c + 1] * inv,
+                                                            oacc[mt][4 * c + 2] * inv, oacc[mt][4 * c + 3] * inv, mw);
       }
-    if (g == 0 && LSE != nullptr) LSE[(int64_t)bh * N + qr] = lt > 0.f ? (m2 + fast_log2(lt)) * kLn2 : kNegInf;
+    if (g == 0 && LSE != nullptr) LSE[(int64_t)bh * N + qr] = mw.lse;
   }
 }
 
-template <bool CAUSAL>
+template <bool CAUSAL, bool MERGE>
 hipError_t run_pp4(const FwdArgs& a, hipStream_t s) {
   constexpr int BR = 16 * 32;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const int total = n_qtiles * a.B * a.H;
-  hipLaunchKernelGGL((fwd_pp4_kernel<CAUSAL>), dim3(total), dim3(1024), 0, s, static_cast<const __bf16*>(a.q),
+  hipLaunchKernelGGL((fwd_pp4_kernel<CAUSAL, MERGE>), dim3(total), dim3(1024), 0, s, static_cast<const __bf16*>(a.q),
                      static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
                      static_cast<__bf16*>(a.o), a.lse, a.N, n_qtiles, total, a.scale * kLog2e);
   return hipGetLastError();
 }
 
-template <int D, int QT, int NBUF, bool CAUSAL>
+template <int D, int QT, int NBUF, bool CAUSAL, bool MERGE>
 hipError_t run_bf16(const FwdArgs& a, hipStream_t s) {
   constexpr int BR = kWaves * 32 * QT;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const int total = n_qtiles * a.B * a.H;
   const float scale_log2 = a.scale * kLog2e;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NBUF, CAUSAL>), dim3(total), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((fwd_bf16_kernel<D, QT, NBUF, CAUSAL, MERGE>), dim3(total), dim3(kThreads), 0, s,
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                      static_cast<const __bf16*>(a.v), static_cast<__bf16*>(a.o), a.lse, a.N, n_qtiles,
                      total, scale_log2);
@@ -753,8 +796,12 @@ hipError_t run_f32(const FwdArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
-  if (a.d == 64) return a.causal ? run_pp4<true>(a, s) : run_pp4<false>(a, s);
-  return a.causal ? run_bf16<128, 1, 2, true>(a, s) : run_bf16<128, 1, 2, false>(a, s);
+  if (a.merge) {
+    if (a.d == 64) return a.causal ? run_pp4<true, true>(a, s) : run_pp4<false, true>(a, s);
+    return a.causal ? run_bf16<128, 1, 2, true, true>(a, s) : run_bf16<128, 1, 2, false, true>(a, s);
+  }
+  if (a.d == 64) return a.causal ? run_pp4<true, false>(a, s) : run_pp4<false, false>(a, s);
+  return a.causal ? run_bf16<128, 1, 2, true, false>(a, s) : run_bf16<128, 1, 2, false, false>(a, s);
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s) {

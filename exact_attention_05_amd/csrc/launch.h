@@ -13,10 +13,11 @@ struct FwdArgs {
   const void* k;
   const void* v;
   void* o;
-  float* lse;  // may be null
+  float* lse;  // may be null (not with merge)
   int B, H, N, d;
   float scale;
   int causal;
+  bool merge = false;  // combine with the running (o, lse) instead of overwriting them
 };
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);

@@ -12,6 +12,7 @@
  *   attn_fwd_splitk_decode_paged
  *                           the same decode over a paged cache addressed
  *                           through a per-sequence block table.
+ *   attn_fwd_merge          the forward combined in place with a running (O, LSE).
  *   attn_bwd                dQ, dK, dV by recomputing P from the saved LSE.
  *   attn_bwd_atomic_dq      the same with dQ accumulated by atomic adds.
  *   attn_quantize_fp8, attn_fwd_fp8
@@ -262,6 +263,32 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const f
 attn_status attn_merge(const void* o_a, const float* lse_a, const void* o_b, const float* lse_b,
                        void* o, float* lse, int B, int H, int N, int d, attn_dtype dtype,
                        void* stream);
+
+/*
+ * attn_fwd_merge -- the forward over this call's keys, combined in place with
+ * a running result over other keys: one step of Ring Attention ("FlashAttention",
+ * xuesongtap.github.io, section 5) with attn_merge's combination fused into
+ * the forward's epilogue.
+ *
+ * On entry (o, lse) hold the result over a key set A (rows with lse = -inf
+ * have seen no key; their o is not read); k, v hold further keys disjoint
+ * from A.  On return (o, lse) hold the result over A and the new keys:
+ *     L = log(e^lse + e^LSE_new),
+ *     o = e^(lse - L) o + e^(LSE_new - L) O_new,  lse = L,
+ * with (O_new, LSE_new) what attn_fwd would compute (O_new is combined in
+ * fp32, before rounding; o is read as stored).  With lse = -inf on entry the
+ * result is attn_fwd's bit for bit.  `causal` masks key j > query i within
+ * this call's block (the diagonal block of a causal sequence).
+ *
+ *   q, k, v : [B, H, N, d] bf16
+ *   o       : [B, H, N, d] bf16, read and written
+ *   lse     : [B, H, N] fp32, read and written (not NULL)
+ *
+ * Supported: ATTN_BF16 with d in {64, 128}.
+ * Errors as attn_fwd; lse NULL is ATTN_ERR_INVALID_ARG.
+ */
+attn_status attn_fwd_merge(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                           int N, int d, attn_dtype dtype, float scale, int causal, void* stream);
 
 /*
  * Workspace size in bytes that attn_bwd needs: 24 bytes per query row

@@ -29,7 +29,7 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("attn_fwd", "attn_fwd_splitk_decode", "attn_fwd_splitk_decode_paged", "attn_bwd",
+    for n in ("attn_fwd", "attn_fwd_merge", "attn_fwd_splitk_decode", "attn_fwd_splitk_decode_paged", "attn_bwd",
               "attn_quantize_fp8", "attn_fwd_fp8", "attn_merge",
               "attn_decode_workspace_bytes",
               "attn_bwd_workspace_bytes", "attn_bwd_atomic_dq", "attn_bwd_atomic_workspace_bytes",
@@ -98,6 +98,25 @@ def test_fwd_validation(args, expect):
         expect = INVALID
     st = lib.attn_fwd(*args, None)
     assert st == expect
+
+
+def test_fwd_merge_validation():
+    lib = _lib()
+    base = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=2, N=64, d=64, dt=BF16, sc=0.125, causal=0)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return lib.attn_fwd_merge(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                                  a["dt"], a["sc"], a["causal"], None)
+
+    assert call(lse=NULL) == INVALID          # the running LSE is read
+    assert call(lse=ctypes.c_void_p(0x10002)) == INVALID
+    assert call(o=MIS) == INVALID
+    assert call(N=0) == INVALID
+    assert call(sc=float("nan")) == INVALID
+    assert call(dt=F32) == UNSUPPORTED        # bf16 only
+    assert call(d=128, dt=F32) == UNSUPPORTED
+    assert call(d=32) == UNSUPPORTED
 
 
 def test_decode_validation():

@@ -1,6 +1,7 @@
-"""GPU parity of attn_merge: results over disjoint key sets merged into the
-result over their union, checked against the oracle's plain attention over
-the union (and against the oracle's merge for hand-made states)."""
+"""GPU parity of attn_merge and attn_fwd_merge: results over disjoint key
+sets merged into the result over their union, checked against the oracle's
+plain attention over the union (and against the oracle's merge for
+hand-made states)."""
 
 import math
 import sys
@@ -9,7 +10,7 @@ import numpy as np
 import pytest
 import torch
 
-from exact_attention_05_amd import attn_fwd, attn_merge
+from exact_attention_05_amd import attn_fwd, attn_fwd_merge, attn_merge
 from exact_attention_05_amd.inputs import make_head, make_tensor, widen
 from oracle import ref_fwd, ref_merge_lse
 
@@ -103,3 +104,78 @@ def test_merge_in_place_and_empty_sides():
     np.testing.assert_allclose(widen(l1), L, rtol=1e-6, atol=1e-6)
     assert_bar("O", widen(o1), O, torch.bfloat16, rel=False)
     assert torch.count_nonzero(o1[:, :, 10:20]) == 0 and torch.isinf(l1[:, :, 10:20]).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("n", [1, 37, 200, 600])
+def test_fwd_merge_two_key_halves(n, d):
+    """attn_fwd over the first half of the keys, then attn_fwd_merge over the
+    second (in place): attention over all of them."""
+    _say(f"fused merge halves n={n} d={d}")
+    seed = 3 * n + d
+    q = make_tensor(seed, "q", 2, 3, n, d, torch.bfloat16, device=DEV)
+    k = make_tensor(seed, "k", 2, 3, 2 * n, d, torch.bfloat16, device=DEV)
+    v = make_tensor(seed, "v", 2, 3, 2 * n, d, torch.bfloat16, device=DEV)
+    scale = 1.0 / math.sqrt(d)
+    half = lambda t, h: t[:, :, h * n:(h + 1) * n].contiguous()
+    o, lse = attn_fwd(q, half(k, 0), half(v, 0), scale=scale)
+    attn_fwd_merge(q, half(k, 1), half(v, 1), o, lse, scale=scale)
+    torch.cuda.synchronize()
+    O, LSE = ref_fwd(widen(q), widen(k), widen(v), scale)
+    assert_bar("O", widen(o), O, torch.bfloat16)
+    assert_lse("LSE", widen(lse), LSE)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_merge_ring_of_causal_shards(d):
+    """The ring of test_ring_of_causal_shards with the merge fused into the
+    forward: causal attention over the whole sequence, and the same result
+    (to the bar) as the forward followed by attn_merge."""
+    G, S, H = 4, 160, 4
+    N = G * S
+    _say(f"fused ring of {G} causal shards d={d}")
+    seed = 60 + d
+    q, k, v = (make_tensor(seed, n, 1, H, N, d, torch.bfloat16, device=DEV) for n in ("q", "k", "v"))
+    shard = lambda t, j: t[:, :, j * S:(j + 1) * S].contiguous()
+    scale = 1.0 / math.sqrt(d)
+    fused, plain = [], []
+    for i in range(G):
+        qi = shard(q, i)
+        o, lse = attn_fwd(qi, shard(k, i), shard(v, i), scale=scale, causal=True)
+        o2, lse2 = o.clone(), lse.clone()
+        for j in range(i - 1, -1, -1):
+            attn_fwd_merge(qi, shard(k, j), shard(v, j), o, lse, scale=scale)
+            oj, lj = attn_fwd(qi, shard(k, j), shard(v, j), scale=scale)
+            attn_merge(o2, lse2, oj, lj, out=o2, lse=lse2)
+        fused.append((o, lse))
+        plain.append((o2, lse2))
+    torch.cuda.synchronize()
+    for h in (0, H - 1):
+        Q, K, V = (widen(make_head(seed, n, 0, h, N, d, torch.bfloat16)) for n in ("q", "k", "v"))
+        O, LSE = ref_fwd(Q, K, V, scale, causal=True)
+        for i, ((o, lse), (o2, lse2)) in enumerate(zip(fused, plain)):
+            rows = slice(i * S, (i + 1) * S)
+            assert_bar(f"O[h{h},shard{i}]", widen(o[0, h]), O[rows], torch.bfloat16)
+            assert_lse(f"LSE[h{h},shard{i}]", widen(lse[0, h]), LSE[rows])
+            assert_bar(f"fused vs plain O[h{h},shard{i}]", widen(o[0, h]), widen(o2[0, h]), torch.bfloat16)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_merge_into_empty_state(d):
+    """A running state with LSE = -inf (and NaN in O, never read) gives
+    attn_fwd's result bit for bit; rows whose running LSE is finite mix."""
+    _say(f"fused merge into empty state d={d}")
+    B, H, N = 1, 2, 300
+    q, k, v = (make_tensor(8 + d, n, B, H, N, d, torch.bfloat16, device=DEV) for n in ("q", "k", "v"))
+    o_ref, lse_ref = attn_fwd(q, k, v, causal=True)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, N), -math.inf, dtype=torch.float32, device=DEV)
+    attn_fwd_merge(q, k, v, o, lse, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o_ref) and torch.equal(lse, lse_ref)
+    # merging the same keys twice: the weights are 1/2 each, O unchanged to
+    # rounding, LSE up by ln 2
+    attn_fwd_merge(q, k, v, o, lse, causal=True)
+    torch.cuda.synchronize()
+    assert_bar("O twice", widen(o), widen(o_ref), torch.bfloat16)
+    np.testing.assert_allclose(widen(lse), widen(lse_ref) + math.log(2.0), rtol=0, atol=1e-5)
