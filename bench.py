@@ -162,7 +162,7 @@ def cpu_baseline_others(budget_s=3.0, max_decode_heads=16):
     import torch
 
     from exact_attention_05_amd.inputs import make_head, widen
-    from oracle import ref_bwd, ref_splitk_decode
+    from oracle import ref_bwd, ref_fwd, ref_splitk_decode
 
     _, cores, _, _ = _host_info()
     out = {}
@@ -193,6 +193,20 @@ def cpu_baseline_others(budget_s=3.0, max_decode_heads=16):
         "value": round(heads * 2.5 * 2.0 * c["N"] ** 2 * c["d"] / t_total / 1e12, 6), "unit": "TFLOP/s",
         "cores": cores, "kind": "oracle",
         "sample": f"{heads} of {c['B'] * c['H']} heads of the causal backward [2,16,4096,64] ({t_total:.1f} s)"}
+    c = FWD_LONG
+    heads, t_total = 0, 0.0
+    while heads < c["B"] * c["H"] and t_total < budget_s:
+        b, h = divmod(heads, c["H"])
+        q, k, v = (widen(make_head(0, n, b, h, c["N"], c["d"], torch.bfloat16, c["input_scale"]))
+                   for n in ("q", "k", "v"))
+        t0 = time.perf_counter()
+        ref_fwd(q[None, None], k[None, None], v[None, None], 1.0 / math.sqrt(c["d"]), True)
+        t_total += time.perf_counter() - t0
+        heads += 1
+    out["fwd_long"] = {
+        "value": round(heads * 2.0 * c["N"] ** 2 * c["d"] / t_total / 1e12, 6), "unit": "TFLOP/s",
+        "cores": cores, "kind": "oracle",
+        "sample": f"{heads} of {c['B'] * c['H']} heads of the causal forward [2,32,8192,128] ({t_total:.1f} s)"}
     return out
 
 
@@ -473,10 +487,27 @@ def main():
             "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
             "traffic": _traffic("decode_d128", ["decode.hip", "common.h"]),
         }
+    if bwd_tf is not None:
+        out["roofline_bwd"] = {
+            "bound": "mfma",
+            "achieved": round(bwd_tf, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(bwd_tf / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+        }
     if "fwd_long" in ms:
         lt = fwd_flops(FWD_LONG) / (ms["fwd_long"] * 1e-3) / 1e12
         out["fwd_long_causal_tflops"] = round(lt, 3)
         out["fwd_long_causal_us"] = round(ms["fwd_long"] * 1e3, 2)
+        out["roofline_fwd_long"] = {
+            "bound": "mfma",
+            "achieved": round(lt, 3),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(lt / PEAK_BF16_TFLOPS, 4),
+            "traffic": _traffic("fwd_bf16_d128_causal", ["fwd.hip", "common.h"]),
+        }
     if "decode_paged" in ms:
         pg = rate("decode_paged", dec_paged_bytes(DEC_PAGED), 1e9)
         out["decode_paged_gbps"] = round(pg, 1)
