@@ -105,3 +105,31 @@ def test_bwd_atomic_causal_workload_sampled():
         assert_bar(f"dQ[{b},{h}]", widen(dq[b, h]), dQ, torch.bfloat16)
         assert_bar(f"dK[{b},{h}]", widen(dk[b, h]), dK, torch.bfloat16)
         assert_bar(f"dV[{b},{h}]", widen(dv[b, h]), dV, torch.bfloat16)
+
+
+def test_bwd_atomic_offsets_beyond_2gib():
+    """Q, K, V, dO [1, H, 256, 64] bf16 spanning more than 2^31 bytes each
+    (the fp32 dQ accumulator more than 2^32): the first and last heads hold
+    seeded data and are checked against the oracle (causal), the others are
+    zero and get zero gradients."""
+    N, d = 256, 64
+    H = (1 << 31) // (N * d * 2) + 16
+    _say(f"bwd atomic offsets beyond 2 GiB: [1,{H},{N},{d}]")
+    seed = 9
+    q, k, v, dO = (torch.zeros((1, H, N, d), dtype=torch.bfloat16, device=DEV) for _ in range(4))
+    for h in (0, H - 1):
+        for t, n in ((q, "q"), (k, "k"), (v, "v"), (dO, "do")):
+            t[0, h].copy_(make_head(seed, n, 0, h, N, d, torch.bfloat16))
+    scale = 0.125
+    o, lse = attn_fwd(q, k, v, scale=scale, causal=True)
+    dq, dk, dv, _ = attn_bwd_atomic_dq(q, k, v, o, dO, lse, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    for h in (0, H - 1):
+        Q, K, V, DO = (widen(make_head(seed, n, 0, h, N, d, torch.bfloat16)) for n in ("q", "k", "v", "do"))
+        dQ, dK, dV = ref_bwd(Q[None, None], K[None, None], V[None, None], DO[None, None], scale, True)
+        assert_bar(f"dQ[{h}]", widen(dq[0, h]), dQ[0, 0], torch.bfloat16)
+        assert_bar(f"dK[{h}]", widen(dk[0, h]), dK[0, 0], torch.bfloat16)
+        assert_bar(f"dV[{h}]", widen(dv[0, h]), dV[0, 0], torch.bfloat16)
+    mid = H // 2
+    for t in (dq, dk, dv):
+        assert torch.count_nonzero(t[0, mid]) == 0

@@ -179,3 +179,37 @@ def test_fwd_merge_into_empty_state(d):
     torch.cuda.synchronize()
     assert_bar("O twice", widen(o), widen(o_ref), torch.bfloat16)
     np.testing.assert_allclose(widen(lse), widen(lse_ref) + math.log(2.0), rtol=0, atol=1e-5)
+
+
+def test_fwd_merge_offsets_beyond_2gib():
+    """attn_fwd_merge over tensors [1, H, 256, 64] bf16 of more than 2^31
+    bytes: the first and last heads hold seeded data (the running result from
+    the first half of the keys, merged with the second half), the others are
+    zero."""
+    N, d = 256, 64
+    H = (1 << 31) // (N * d * 2) + 16
+    _say(f"fused merge offsets beyond 2 GiB: [1,{H},{N},{d}]")
+    seed = 10
+    q, k, v = (torch.zeros((1, H, N, d), dtype=torch.bfloat16, device=DEV) for _ in range(3))
+    k2, v2 = torch.zeros_like(k), torch.zeros_like(v)
+    for h in (0, H - 1):
+        q[0, h].copy_(make_head(seed, "q", 0, h, N, d, torch.bfloat16))
+        kk = make_head(seed, "k", 0, h, 2 * N, d, torch.bfloat16)
+        vv = make_head(seed, "v", 0, h, 2 * N, d, torch.bfloat16)
+        k[0, h].copy_(kk[:N])
+        v[0, h].copy_(vv[:N])
+        k2[0, h].copy_(kk[N:])
+        v2[0, h].copy_(vv[N:])
+    o, lse = attn_fwd(q, k, v, scale=0.125)
+    attn_fwd_merge(q, k2, v2, o, lse, scale=0.125)
+    torch.cuda.synchronize()
+    for h in (0, H - 1):
+        Q = widen(make_head(seed, "q", 0, h, N, d, torch.bfloat16))
+        K = widen(make_head(seed, "k", 0, h, 2 * N, d, torch.bfloat16))
+        V = widen(make_head(seed, "v", 0, h, 2 * N, d, torch.bfloat16))
+        O, LSE = ref_fwd(Q[None, None], K[None, None], V[None, None], 0.125)
+        assert_bar(f"O[{h}]", widen(o[0, h]), O[0, 0], torch.bfloat16)
+        assert_lse(f"LSE[{h}]", widen(lse[0, h]), LSE[0, 0])
+    mid = H // 2
+    assert torch.count_nonzero(o[0, mid]) == 0
+    np.testing.assert_allclose(widen(lse[0, mid]), np.log(2 * N), rtol=0, atol=1e-5)
