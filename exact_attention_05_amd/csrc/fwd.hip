@@ -29,6 +29,9 @@
 //   * the causal mask is -inf on the diagonal tiles only; tiles above the
 //     diagonal are never loaded, and the longest query tiles are dispatched
 //     first (Triton tutorial, section 8.7.1).
+//   * attn_fwd_merge instantiates the same kernels with MERGE: the epilogue
+//     reads the row's running (O, LSE) and writes the result over both key
+//     sets (see merge_weights), so a Ring Attention step is one launch.
 #include "common.h"
 #include "launch.h"
 
