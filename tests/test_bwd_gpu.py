@@ -13,7 +13,7 @@ import torch
 
 from exact_attention_05_amd import attn_bwd, attn_fwd
 from exact_attention_05_amd.inputs import make_head, make_tensor, widen
-from oracle import ref_bwd, ref_fwd
+from oracle import ref_bwd
 
 from helpers import assert_bar
 

@@ -11,7 +11,6 @@ outputs, and every replay is compared with that eager pass (bit for bit,
 except the atomic dQ, whose fp32 summation order varies: to the bf16 bar).
 """
 
-import math
 import sys
 
 import pytest
