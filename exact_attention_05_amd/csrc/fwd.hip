@@ -9,9 +9,10 @@
 // Mapping to the hardware:
 //   * every wavefront owns 32 whole query rows (split-Q, "FlashAttention 1 和
 //     FlashAttention 2 的区别", sections 7-8), so no cross-wave merge exists;
-//     d = 128: 4 wavefronts per workgroup (fwd_bf16_kernel); d = 64: 16
-//     wavefronts, four per SIMD in two groups one phase apart, so matrix and
-//     vector work of different wavefronts overlap (fwd_pp4_kernel);
+//     d = 128: 4 wavefronts per workgroup (fwd_bf16_kernel); d = 64: 8
+//     wavefronts in two groups one phase apart, two workgroups per CU (four
+//     wavefronts per SIMD), so matrix and vector work of different
+//     wavefronts overlap (fwd_pp4_kernel);
 //   * Q stays in VGPRs as MFMA B operands for the whole K/V sweep;
 //   * K/V tiles of 64 keys go HBM -> LDS with direct-to-LDS copies into a
 //     ring of buffers in the swizzled tile layout of common.h, copied ahead
@@ -551,29 +552,33 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// d = 64 forward, four wavefronts per SIMD.  Sixteen wavefronts of 32 query
-// rows (512 rows per workgroup); wavefronts 0-7 lead and 8-15 trail by one
-// phase, so on every SIMD two wavefronts are in a matrix phase while two are
-// in a vector phase.  A single wavefront can issue only a fraction of what a
-// SIMD executes -- about three quarters of the MFMA rate and half of the VALU
-// rate -- so two of each kind keep both units busy.  Per 64-key tile j:
+// d = 64 forward, four wavefronts per SIMD.  Eight wavefronts of 32 query
+// rows (256 rows per workgroup); wavefronts 0-3 lead and 4-7 trail by one
+// phase, so on every SIMD one wavefront of the workgroup is in a matrix phase
+// while the other is in a vector phase, and two workgroups share each CU (80
+// KB of LDS each), drifting freely against each other.  A single wavefront
+// can issue only a fraction of what a SIMD executes -- about three quarters of
+// the MFMA rate and half of the VALU rate -- so four per SIMD keep both units
+// busier; with two workgroups each barrier holds 8 wavefronts, not 16, and
+// the shorter query tiles balance causal grids better.  Per 64-key tile j:
 // M(j) = O^T += V_{j-1}^T P~_{j-1}^T, then S_j^T = K_j Q^T (operands read from
 // LDS in the phase); V(j) = mask, exponentials, bf16 P~, row sums.
 //
 // Ring of 5 tile buffers (K | V): tile j+3 is copied at M(j) into the slot of
-// tile j-2, whose last reader (the trail's M(j-1)) is one phase earlier.
+// tile j-2, whose last reader (the trail's M(j-1)) is one phase earlier; each
+// wavefront copies 1 KB of the K tile and 1 KB of the V tile.
 // Each wavefront waits for its own copies of tile j+1 before the barrier that
 // opens its V(j); for the trail that barrier opens the lead's M(j+1), the
 // first reader of tile j+1.  Online state and reference rule as in
 // fwd_bf16_kernel.
 // ---------------------------------------------------------------------------
 template <bool CAUSAL, bool MERGE = false>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void fwd_pp4_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void fwd_pp4_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
     __bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg, float scale_log2) {
   constexpr int D = 64;
   using T = TileLayout<D>;
-  constexpr int NW = 16;
+  constexpr int NW = 8;
   constexpr int BR = NW * 32;
   __shared__ __attribute__((aligned(1024))) unsigned char sb0[2 * T::kBytes];
   __shared__ __attribute__((aligned(1024))) unsigned char sb1[2 * T::kBytes];
@@ -598,12 +603,12 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   const int kend = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kend + kBc - 1) / kBc;
 
-  // wavefronts 0-7 copy the K tile, 8-15 the V tile: one 1 KB copy each
-  const TileCopy<D, 8> cp(wave & 7, lane);
-  const __bf16* csrc = (wave < 8 ? K : V) + base;
-  const int coff = wave < 8 ? 0 : T::kBytes;
+  // each wavefront copies one 1 KB piece of the K tile and one of the V tile
+  // (two direct-to-LDS copies per tile)
+  const TileCopy<D, NW> cp(wave, lane);
   auto issue_tile = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
-    cp.issue(csrc, j * kBc, N, buf + coff);
+    cp.issue(K + base, j * kBc, N, buf);
+    cp.issue(V + base, j * kBc, N, buf + T::kBytes);
   };
 
   issue_tile(0, sb0);
@@ -705,13 +710,13 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
   };
 
   // Tile 0 must have landed before the first barrier (tiles 1 and 2 may not).
-  if (ntiles > 2) wait_vm_at_most<2>(); else if (ntiles > 1) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
+  if (ntiles > 2) wait_vm_at_most<4>(); else if (ntiles > 1) wait_vm_at_most<2>(); else wait_vm_at_most<0>();
   lds_barrier();
   if (!lead) lds_barrier();
   if (ntiles > 3) issue_tile(3, sb3);
   mph(sb0, sb0, false, true);
   // tile 1 (tiles 2 and 3 may still be in flight)
-  if (ntiles > 3) wait_vm_at_most<2>(); else if (ntiles > 2) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
+  if (ntiles > 3) wait_vm_at_most<4>(); else if (ntiles > 2) wait_vm_at_most<2>(); else wait_vm_at_most<0>();
   lds_barrier();
   vph(0, sb0);
   // Tile j at cur, j-1 at prev; tile j+3 goes to far.
@@ -721,7 +726,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
     if (j + 3 < ntiles) issue_tile(j + 3, far);
     mph(cur, prev, true, true);
     // tile j+1 (tiles j+2 and j+3 may still be in flight)
-    if (j + 3 < ntiles) wait_vm_at_most<2>(); else if (j + 2 < ntiles) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
+    if (j + 3 < ntiles) wait_vm_at_most<4>(); else if (j + 2 < ntiles) wait_vm_at_most<2>(); else wait_vm_at_most<0>();
     lds_barrier();
     vph(j, cur);
   };
@@ -762,10 +767,10 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
 
 template <bool CAUSAL, bool MERGE>
 hipError_t run_pp4(const FwdArgs& a, hipStream_t s) {
-  constexpr int BR = 16 * 32;
+  constexpr int BR = 8 * 32;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const int total = n_qtiles * a.B * a.H;
-  hipLaunchKernelGGL((fwd_pp4_kernel<CAUSAL, MERGE>), dim3(total), dim3(1024), 0, s, static_cast<const __bf16*>(a.q),
+  hipLaunchKernelGGL((fwd_pp4_kernel<CAUSAL, MERGE>), dim3(total), dim3(512), 0, s, static_cast<const __bf16*>(a.q),
                      static_cast<const __bf16*>(a.k), static_cast<const __bf16*>(a.v),
                      static_cast<__bf16*>(a.o), a.lse, a.N, n_qtiles, total, a.scale * kLog2e);
   return hipGetLastError();
