@@ -72,7 +72,9 @@ __device__ __forceinline__ constexpr int pkey(int h, int J) { return 32 * (J >> 
 
 // ---------------------------------------------------------------------------
 // Forward kernel, d = 64.  Work ids, ring of five tiles, phase structure and
-// barriers as fwd_pp4_kernel; waves 0-3 copy the K tile and 4-7 the V tile.
+// barriers as fwd_pp4_kernel, with sixteen wavefronts (512 query rows) per
+// workgroup and one workgroup per CU; waves 0-3 copy the K tile and 4-7 the
+// V tile.
 // ---------------------------------------------------------------------------
 template <bool CAUSAL>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void fwd_fp8_kernel(
