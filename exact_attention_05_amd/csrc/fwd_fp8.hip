@@ -71,19 +71,19 @@ __device__ __forceinline__ int fp8_off(int k, int c) { return 64 * k + 16 * (c ^
 __device__ __forceinline__ constexpr int pkey(int h, int J) { return 32 * (J >> 4) + acc_row(J & 15, h); }
 
 // ---------------------------------------------------------------------------
-// Forward kernel, d = 64.  Work ids, ring of five tiles, phase structure and
-// barriers as fwd_pp4_kernel, with sixteen wavefronts (512 query rows) per
-// workgroup and one workgroup per CU; waves 0-3 copy the K tile and 4-7 the
-// V tile.
+// Forward kernel, d = 64.  Work ids, eight wavefronts (256 query rows) per
+// workgroup and two workgroups per CU, ring of five tiles, phase structure
+// and barriers as fwd_pp4_kernel; waves 0-3 copy the K tile and 4-7 the V
+// tile.
 // ---------------------------------------------------------------------------
 template <bool CAUSAL>
-__global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) void fwd_fp8_kernel(
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
     __bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg, int block_m,
     int block_n, float scale_log2) {
   constexpr int D = 64;
-  constexpr int NW = 16;
+  constexpr int NW = 8;
   constexpr int BR = NW * 32;
   constexpr int TB = 2 * kFp8Tile;  // K | V
   __shared__ __attribute__((aligned(1024))) unsigned char sb0[TB];
@@ -114,7 +114,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4, 4))) vo
 
   // copy geometry: waves 0-3 fill the K tile, 4-7 the V tile, 1 KB each;
   // lane l fills physical chunk l % 4 of row 16 (wave % 4) + l / 4.
-  const bool copier = wave < 8;
+  const bool copier = wave < 8;  // every wavefront of the workgroup
   const uint8_t* csrc = (wave < 4 ? K : V) + base;  // wave-uniform
   const int crow = 16 * (wave & 3) + (lane >> 2);
   const int ccol = 16 * ((lane & 3) ^ ((crow >> 2) & 3));
@@ -475,10 +475,10 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const __bf16* __restrict
 
 template <bool CAUSAL>
 hipError_t run_fp8(const Fp8FwdArgs& a, hipStream_t s) {
-  constexpr int BR = 16 * 32;
+  constexpr int BR = 8 * 32;
   const int n_qtiles = (a.N + BR - 1) / BR;
   const int total = n_qtiles * a.B * a.H;
-  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL>), dim3(total), dim3(1024), 0, s, static_cast<const uint8_t*>(a.q),
+  hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL>), dim3(total), dim3(512), 0, s, static_cast<const uint8_t*>(a.q),
                      static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), a.q_scale, a.k_scale,
                      a.v_scale, static_cast<__bf16*>(a.o), a.lse, a.N, n_qtiles, total, a.block_m, a.block_n,
                      a.scale * kLog2e);
