@@ -56,7 +56,7 @@ def test_worked_example(scale, qmul):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 4, 17, 64, 100, 129, 300])
+@pytest.mark.parametrize("N", [1, 4, 17, 64, 100, 129, 300, 555, 1100])
 def test_bf16_ragged(N, d, causal):
     _say(f"bf16 N={N} d={d} causal={causal}")
     q, k, v = _inputs(N * 7 + d, 2, 3, N, d, torch.bfloat16)
