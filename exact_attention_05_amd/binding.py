@@ -186,15 +186,30 @@ def attn_fwd_splitk_decode(q, k_cache, v_cache, num_splits, scale=None, out=None
     need = attn_decode_workspace_bytes(B, H, d, num_splits)
     if workspace is None:
         workspace = torch.empty((max(need, 4) + 3) // 4, dtype=torch.float32, device=dev)
-    if out is None:
-        out = torch.empty_like(q)
-    if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    else:
+        _require(workspace.is_cuda and workspace.device == dev, f"workspace must be on {dev}")
+        _require(workspace.is_contiguous(), "workspace must be contiguous")
+    out, lse = _decode_outputs(q, out, lse)
     st = _load().attn_fwd_splitk_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
                                         _ptr(workspace), workspace.numel() * workspace.element_size(),
                                         B, H, L, d, int(num_splits), _dtype_code(q), scale, _stream(dev))
     _check(st, "attn_fwd_splitk_decode")
     return out, lse, workspace
+
+
+def _decode_outputs(q, out, lse):
+    """The decode's (o [B, H, 1, d], lse [B, H] fp32): checked when given, else new."""
+    B, H, _, d = q.shape
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_bhnd("out", out, (B, H, 1, d), q.dtype, dev)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=dev)
+    else:
+        _check_bhnd("lse", lse, (B, H), torch.float32, dev)
+    return out, lse
 
 
 def attn_fwd_splitk_decode_paged(q, k_pool, v_pool, block_table, seq_lens, num_splits, scale=None, out=None,
@@ -374,12 +389,17 @@ def _bwd_call(entry, q, k, v, o, dO, lse, scale, causal, dq, dk, dv, workspace):
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_bhnd(name, t, (B, H, N, d), q.dtype, dev)
     if entry == "attn_bwd":
         need = attn_bwd_workspace_bytes(B, H, N)
     else:
         need = attn_bwd_atomic_workspace_bytes(B, H, N, d)
     if workspace is None:
         workspace = torch.empty((need + 3) // 4, dtype=torch.float32, device=dev)
+    else:
+        _require(workspace.is_cuda and workspace.device == dev, f"workspace must be on {dev}")
+        _require(workspace.is_contiguous(), "workspace must be contiguous")
     st = getattr(_load(), entry)(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dO), _ptr(lse), _ptr(dq), _ptr(dk),
                                  _ptr(dv), _ptr(workspace), workspace.numel() * workspace.element_size(),
                                  B, H, N, d, _dtype_code(q), scale, int(bool(causal)), _stream(dev))

@@ -42,8 +42,10 @@ def _gpu_bwd(q, k, v, dO, scale, causal, want_lse=False):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 17, 64, 100, 129, 200])
+@pytest.mark.parametrize("N", [1, 17, 64, 100, 129, 200, 300, 555, 1100])
 def test_bwd_ragged(N, d, causal):
+    """Every gradient against the oracle; the longer lengths span 2-5 key
+    and query workgroups of both passes with a ragged last one."""
     _say(f"bwd N={N} d={d} causal={causal}")
     q, k, v, dO = _inputs(N + d, 1, 2, N, d)
     scale = 1.0 / math.sqrt(d)

@@ -198,6 +198,24 @@ def test_long_causal_workload_sampled():
         assert_lse(f"LSE[{b},{h}]", widen(lse[b, h, rows]), LSE)
 
 
+def test_long_causal_workload_full_head():
+    """One whole head of the long causal workload (bf16 [2, 32, 8192, 128],
+    inputs N(0, 1) x 0.5): every one of its 8192 rows against the oracle,
+    from a launch over all 64 heads."""
+    B, H, N, d = 2, 32, 8192, 128
+    seed = 0
+    b, h = 1, 20
+    _say(f"workload [{B},{H},{N},{d}] causal, full head ({b},{h})")
+    q, k, v = (make_tensor(seed, n, B, H, N, d, torch.bfloat16, 0.5, device=DEV) for n in ("q", "k", "v"))
+    scale = 1.0 / math.sqrt(d)
+    o, lse = attn_fwd(q, k, v, scale=scale, causal=True)
+    torch.cuda.synchronize()
+    qh, kh, vh = (widen(make_head(seed, n, b, h, N, d, torch.bfloat16, 0.5)) for n in ("q", "k", "v"))
+    O, LSE = ref_fwd(qh, kh, vh, scale, True)
+    assert_bar(f"O[{b},{h}]", widen(o[b, h]), O, torch.bfloat16)
+    assert_lse(f"LSE[{b},{h}]", widen(lse[b, h]), LSE)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_offsets_beyond_2gib(d):
     """Each tensor spans more than 2^31 bytes ([1, H, 256, d] bf16 with
