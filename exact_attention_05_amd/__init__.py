@@ -11,6 +11,7 @@ __all__ = [
     "attn_fwd_merge",
     "attn_fwd_splitk_decode",
     "attn_fwd_splitk_decode_paged",
+    "attn_fwd_splitk_decode_noalloc",
     "attn_bwd",
     "attn_bwd_atomic_dq",
     "attn_quantize_fp8",

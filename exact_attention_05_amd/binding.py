@@ -22,6 +22,7 @@ _STATUS_NAMES = {
     2: "ATTN_ERR_UNSUPPORTED",
     3: "ATTN_ERR_WORKSPACE",
     4: "ATTN_ERR_HIP",
+    5: "ATTN_ERR_SCRATCH",
 }
 ATTN_F32 = 0
 ATTN_BF16 = 1
@@ -62,6 +63,8 @@ def _load():
     lib.attn_decode_workspace_bytes.argtypes = [ci, ci, ci, ci]
     lib.attn_fwd_splitk_decode.restype = ci
     lib.attn_fwd_splitk_decode.argtypes = [vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, cf, vp]
+    lib.attn_fwd_splitk_decode_noalloc.restype = ci
+    lib.attn_fwd_splitk_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, ci, ci, ci, ci, ci, ci, cf, vp]
     lib.attn_fwd_splitk_decode_paged.restype = ci
     lib.attn_fwd_splitk_decode_paged.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, sz, ci, ci, ci, ci, ci, ci, ci,
                                                  ci, cf, vp]
@@ -209,6 +212,31 @@ def _decode_outputs(q, out, lse):
         lse = torch.empty((B, H), dtype=torch.float32, device=dev)
     else:
         _check_bhnd("lse", lse, (B, H), torch.float32, dev)
+    return out, lse
+
+
+def attn_fwd_splitk_decode_noalloc(q, k_cache, v_cache, num_splits, scale=None, out=None, lse=None):
+    """attn_fwd_splitk_decode without a workspace: the library keeps the
+    partials in its fixed per-device scratch (ATTN_DECODE_SCRATCH_BYTES) and
+    allocates nothing.  With ``out`` and ``lse`` given, this call allocates
+    no device memory at all.  Calls that may overlap on one GPU race.
+
+    Returns (o [B, H, 1, d], lse [B, H]).
+    """
+    B, H, one, d = q.shape
+    _require(one == 1, "q must be [B, H, 1, d]")
+    L = k_cache.shape[2]
+    dev = q.device
+    _check_bhnd("q", q, (B, H, 1, d), q.dtype, dev)
+    _check_bhnd("k_cache", k_cache, (B, H, L, d), q.dtype, dev)
+    _check_bhnd("v_cache", v_cache, (B, H, L, d), q.dtype, dev)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    out, lse = _decode_outputs(q, out, lse)
+    with torch.cuda.device(dev):
+        st = _load().attn_fwd_splitk_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(lse),
+                                                    B, H, L, d, int(num_splits), _dtype_code(q), scale,
+                                                    _stream(dev))
+    _check(st, "attn_fwd_splitk_decode_noalloc")
     return out, lse
 
 

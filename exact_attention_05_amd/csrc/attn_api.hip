@@ -45,6 +45,8 @@ const char* attn_status_string(attn_status s) {
       return "ATTN_ERR_WORKSPACE: workspace missing or too small";
     case ATTN_ERR_HIP:
       return "ATTN_ERR_HIP: kernel launch failed";
+    case ATTN_ERR_SCRATCH:
+      return "ATTN_ERR_SCRATCH: the call needs more than the library's fixed scratch (ATTN_DECODE_SCRATCH_BYTES)";
   }
   return "unknown attn_status";
 }
@@ -97,6 +99,23 @@ attn_status attn_fwd_splitk_decode(const void* q, const void* k_cache, const voi
   if (workspace_bytes < attn_decode_workspace_bytes(B, H, d, num_splits)) return ATTN_ERR_WORKSPACE;
   attn::DecodeArgs a{q, k_cache, v_cache, o, lse, static_cast<float*>(workspace), B, H, L, d, num_splits, scale};
   return from_hip(attn::launch_decode_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
+attn_status attn_fwd_splitk_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, void* o,
+                                           float* lse, int B, int H, int L, int d, int num_splits, attn_dtype dtype,
+                                           float scale, void* stream) {
+  static_assert(ATTN_DECODE_SCRATCH_BYTES == attn::kDecodeScratchBytes, "scratch size");
+  if (B < 1 || H < 1 || L < 1 || L > (1 << 30) || d < 1) return ATTN_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > 65535) return ATTN_ERR_INVALID_ARG;
+  if ((int64_t)B * H * num_splits > INT32_MAX) return ATTN_ERR_INVALID_ARG;
+  if (!good_scale(scale)) return ATTN_ERR_INVALID_ARG;
+  if (dtype != ATTN_F32 && dtype != ATTN_BF16) return ATTN_ERR_INVALID_ARG;
+  if (!tensor_ok(q) || !tensor_ok(k_cache) || !tensor_ok(v_cache) || !tensor_ok(o)) return ATTN_ERR_INVALID_ARG;
+  if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
+  if (!(dtype == ATTN_BF16 && (d == 64 || d == 128))) return ATTN_ERR_UNSUPPORTED;
+  if (attn_decode_workspace_bytes(B, H, d, num_splits) > ATTN_DECODE_SCRATCH_BYTES) return ATTN_ERR_SCRATCH;
+  attn::DecodeArgs a{q, k_cache, v_cache, o, lse, nullptr, B, H, L, d, num_splits, scale};
+  return from_hip(attn::launch_decode_noalloc_bf16(a, static_cast<hipStream_t>(stream)));
 }
 
 attn_status attn_fwd_splitk_decode_paged(const void* q, const void* k_pool, const void* v_pool,

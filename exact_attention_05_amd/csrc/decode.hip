@@ -17,6 +17,8 @@
 // Reduce step (decode_merge_kernel): one workgroup per (b, h) merges its S
 // partials: m = max m_c, l = sum e^(m_c - m) l_c, U = sum e^(m_c - m) U_c,
 // O = U / l, LSE = m + ln l.
+#include <atomic>
+
 #include "common.h"
 #include "launch.h"
 
@@ -327,6 +329,48 @@ hipError_t launch_decode_bf16(const DecodeArgs& a, hipStream_t s) {
 hipError_t launch_decode_paged_bf16(const DecodeArgs& a, const PagedArgs& p, hipStream_t s) {
   const PagedKV pg{p.block_table, p.seq_lens, a.H, p.max_blocks, p.num_blocks, p.log2_bs};
   return a.d == 64 ? run_decode<64, true>(a, pg, s) : run_decode<128, true>(a, pg, s);
+}
+
+// ---------------------------------------------------------------------------
+// The decode without allocation.  Its partials go to `scratch`, a fixed array
+// that each device holds for the life of the process, so the call needs no
+// workspace from the caller.  In host code `scratch` names a host-side
+// stand-in, not device memory: its device address is looked up once per
+// device with hipGetSymbolAddress and only that address reaches the kernels.
+// The partial kernel writes every (U, m, l) entry that the merge kernel reads,
+// so nothing has to be cleared between calls.
+// ---------------------------------------------------------------------------
+namespace {
+static __device__ __align__(256) float scratch[kDecodeScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<float*> g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch (looked up on first use).
+hipError_t scratch_address(float** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (addr == nullptr) return hipErrorInvalidSymbol;
+    p = static_cast<float*>(addr);
+    g_scratch[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_decode_noalloc_bf16(const DecodeArgs& a, hipStream_t s) {
+  DecodeArgs b = a;
+  hipError_t e = scratch_address(&b.ws);
+  if (e != hipSuccess) return e;
+  return launch_decode_bf16(b, s);
 }
 
 }  // namespace attn

@@ -45,6 +45,12 @@ struct PagedArgs {
 
 hipError_t launch_decode_paged_bf16(const DecodeArgs& a, const PagedArgs& p, hipStream_t s);
 
+// The dense decode with its partials in a fixed per-device scratch of
+// kDecodeScratchBytes (a.ws is ignored); the caller has checked that the
+// partials fit.  Calls that overlap on one device share the scratch and race.
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+hipError_t launch_decode_noalloc_bf16(const DecodeArgs& a, hipStream_t s);
+
 // FP8 forward: q, k, v are E4M3 [B, H, N, d]; scales are powers of two per
 // block of rows (block_m for Q, block_n for K and V); o is bf16.
 struct Fp8FwdArgs {

@@ -57,7 +57,8 @@ typedef enum {
   ATTN_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, bad scale */
   ATTN_ERR_UNSUPPORTED = 2, /* dtype/head_dim combination not built */
   ATTN_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
-  ATTN_ERR_HIP = 4          /* a HIP launch reported an error */
+  ATTN_ERR_HIP = 4,         /* a HIP launch reported an error */
+  ATTN_ERR_SCRATCH = 5      /* a no-allocation call needs more than the fixed scratch */
 } attn_status;
 
 typedef enum { ATTN_F32 = 0, ATTN_BF16 = 1 } attn_dtype;
@@ -132,6 +133,37 @@ attn_status attn_fwd_splitk_decode(const void* q, const void* k_cache, const voi
                                    void* o, float* lse, void* workspace, size_t workspace_bytes,
                                    int B, int H, int L, int d, int num_splits, attn_dtype dtype,
                                    float scale, void* stream);
+
+/* Size of the fixed per-device scratch of attn_fwd_splitk_decode_noalloc. */
+#define ATTN_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+
+/*
+ * attn_fwd_splitk_decode_noalloc -- attn_fwd_splitk_decode for callers that
+ * cannot allocate device memory (code under HIP graph capture, allocation-free
+ * serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same operation, arguments and result as attn_fwd_splitk_decode, without the
+ * workspace: the chunk partials go to a fixed scratch array of
+ * ATTN_DECODE_SCRATCH_BYTES (32 MiB) that the library keeps on each device it
+ * runs on until the process ends.  The call allocates nothing and uses the
+ * scratch of the CURRENT device (hipGetDevice); `stream` must belong to that
+ * device.  The scratch is not readable by the caller.
+ *
+ * Every call on a device shares that device's scratch: calls whose kernels
+ * may overlap on one device (on different streams without ordering between
+ * them) race and give undefined results.  Calls on one stream are ordered.
+ *
+ * Limit: attn_decode_workspace_bytes(B, H, d, num_splits) must not exceed
+ * ATTN_DECODE_SCRATCH_BYTES, i.e. B*H*num_splits*(d + 2) <= 8388608; for
+ * B*H = 512 and d = 128 that is up to 126 splits.
+ *
+ * Errors as attn_fwd_splitk_decode (no workspace errors), plus
+ * ATTN_ERR_SCRATCH when the partials would not fit in the scratch (checked on
+ * the host; nothing is launched).
+ */
+attn_status attn_fwd_splitk_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                           void* o, float* lse, int B, int H, int L, int d,
+                                           int num_splits, attn_dtype dtype, float scale, void* stream);
 
 /*
  * attn_fwd_splitk_decode_paged -- the split-K decode of

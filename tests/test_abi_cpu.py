@@ -29,7 +29,8 @@ def _declared_functions():
 
 def test_header_declares_the_boundary():
     names = _declared_functions()
-    for n in ("attn_fwd", "attn_fwd_merge", "attn_fwd_splitk_decode", "attn_fwd_splitk_decode_paged", "attn_bwd",
+    for n in ("attn_fwd", "attn_fwd_merge", "attn_fwd_splitk_decode", "attn_fwd_splitk_decode_paged",
+              "attn_fwd_splitk_decode_noalloc", "attn_bwd",
               "attn_quantize_fp8", "attn_fwd_fp8", "attn_merge",
               "attn_decode_workspace_bytes",
               "attn_bwd_workspace_bytes", "attn_bwd_atomic_dq", "attn_bwd_atomic_workspace_bytes",
@@ -43,7 +44,7 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, n), f"missing export {n}"
 
 
-OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR = 0, 1, 2, 3, 4
+OK, INVALID, UNSUPPORTED, WORKSPACE, HIPERR, SCRATCH = 0, 1, 2, 3, 4, 5
 F32, BF16 = 0, 1
 P = ctypes.c_void_p(0x10000)          # fake, 16-byte aligned; never dereferenced
 MIS = ctypes.c_void_p(0x10008)        # 8-byte aligned only
@@ -52,7 +53,7 @@ NULL = None
 
 def test_status_strings_and_version():
     lib = _lib()
-    for code in range(5):
+    for code in range(6):
         s = lib.attn_status_string(code).decode()
         assert s.startswith("ATTN_")
     assert lib.attn_status_string(99).decode().startswith("unknown")
@@ -142,6 +143,34 @@ def test_decode_validation():
     assert call(ws=NULL) == WORKSPACE
     assert call(ws=MIS) == WORKSPACE
     assert call(wsb=ws_need - 1) == WORKSPACE
+
+
+def test_decode_noalloc_validation():
+    lib = _lib()
+    f = lib.attn_fwd_splitk_decode_noalloc
+    base = dict(q=P, k=P, v=P, o=P, lse=NULL, B=16, H=32, L=100, d=128, S=126, dt=BF16, sc=0.1)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["L"], a["d"], a["S"], a["dt"], a["sc"],
+                 None)
+
+    assert call(q=NULL) == INVALID
+    assert call(o=MIS) == INVALID
+    assert call(lse=ctypes.c_void_p(0x10002)) == INVALID
+    assert call(L=0) == INVALID
+    assert call(S=0) == INVALID
+    assert call(sc=float("inf")) == INVALID
+    assert call(d=96) == UNSUPPORTED
+    assert call(dt=F32) == UNSUPPORTED
+    # the partials B*H*S*(d+2) fp32 values must fit in the fixed 32 MiB scratch:
+    # 512 heads at d = 128 fit 126 splits, not 127
+    assert lib.attn_decode_workspace_bytes(16, 32, 128, 126) <= 32 << 20
+    assert lib.attn_decode_workspace_bytes(16, 32, 128, 127) > 32 << 20
+    assert call(S=127) == SCRATCH
+    assert call(S=256) == SCRATCH
+    assert call(B=2, H=1, d=128, S=65535) == SCRATCH
+    assert lib.attn_status_string(SCRATCH).decode().startswith("ATTN_ERR_SCRATCH")
 
 
 def test_paged_decode_validation():
