@@ -43,7 +43,7 @@ from .attention_ref import (  # noqa: F401
     gather_paged_rows,
     ref_paged_decode,
     e4m3_round,
-    pow2_block_scale,
+    fp8_block_scale,
     hadamard_rotate,
     quantize_fp8_blocks,
     ref_fwd_fp8,

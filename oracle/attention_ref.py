@@ -319,7 +319,6 @@ def ref_paged_decode(q, k_pool, v_pool, block_table, seq_lens, scale):
 # ---------------------------------------------------------------------------
 
 E4M3_MAX = 448.0
-P_EXP = 3  # P~ is quantised as e4m3(2^(u - M + P_EXP) * r), see ref_fwd_fp8
 
 
 def e4m3_round(x):
@@ -353,38 +352,36 @@ def hadamard_rotate(x, signs):
     return (x * _f64(signs)) @ H / np.sqrt(d)
 
 
-def pow2_block_scale(amax):
-    """The block scale: the smallest power of two 2^k with 448 2^k >= amax
-    (1 for an all-zero block), so amax / scale lies in (224, 448].  The
-    page takes scale = max|x| / 448 ([Triton-ch8] section 8.9.4); a power of
-    two keeps x / scale exact and lets the matrix unit apply the scale.  The
-    exponent is kept in [-126, 127] (normal fp32 numbers), so blocks with
-    amax < 448 2^-126 use fewer than the top binade."""
-    amax = float(amax)
-    if amax == 0.0:
+def fp8_block_scale(amax):
+    """A block's scale, max|x| / 448 ([Triton-ch8] section 8.9.4), evaluated
+    in fp32 as the page's PyTorch code does (amax is an fp32 value; the
+    quotient is IEEE fp32 division, correctly rounded).  An all-zero block,
+    where the page's quotient would be 0 and x / scale undefined, gets 1 (any
+    positive scale turns it into zero codes).  Returns a Python float holding
+    the fp32 value."""
+    a = np.float32(amax)
+    if a == 0:
         return 1.0
-    k = int(np.ceil(np.log2(amax / E4M3_MAX)))
-    while E4M3_MAX * 2.0 ** (k - 1) >= amax:     # exact comparisons fix a misrounded log
-        k -= 1
-    while E4M3_MAX * 2.0 ** k < amax:
-        k += 1
-    return 2.0 ** max(k, -126)
+    return float(a / np.float32(E4M3_MAX))
 
 
 def quantize_fp8_blocks(x, block_rows, signs=None):
-    """Per-block FP8 quantisation ([Triton-ch8] sections 8.9.3-8.9.4).
+    """Per-block FP8 quantisation, the page's quantize_to_fp8 ([Triton-ch8]
+    sections 8.9.3-8.9.4) with its block scales.
 
-    x: [..., N, d].  Rows are grouped into blocks of ``block_rows``; each
-    block gets scale = pow2_block_scale(max|x|) and codes
-    e4m3(clamp(x / scale, +-448)).  With ``signs`` the rows are first rotated
-    by hadamard_rotate and rounded to fp32 (the precision the values are
-    held in before the division).  Returns (values [..., N, d] float64 --
-    the e4m3 values, exactly --, scales [..., ceil(N / block_rows)]).
+    x: [..., N, d] (values that fp32 holds exactly, e.g. bf16).  Rows are
+    grouped into blocks of ``block_rows``; each block gets
+    scale = fp8_block_scale(max|x|) and codes e4m3(clamp(x / scale, +-448)),
+    x / scale divided in fp32 like the page's tensor code.  With ``signs``
+    the rows are first rotated by hadamard_rotate and rounded to fp32 (the
+    precision the values are held in before the division).  Returns
+    (values [..., N, d] float64 -- the e4m3 values, exactly --,
+    scales [..., ceil(N / block_rows)] -- fp32 values held in float64).
     """
     x = _f64(x)
     if signs is not None:
         x = hadamard_rotate(x, signs)
-    x32 = x.astype(np.float32).astype(np.float64)
+    x32 = x.astype(np.float32)
     N = x.shape[-2]
     nb = -(-N // block_rows)
     vals = np.zeros(x.shape)
@@ -392,8 +389,9 @@ def quantize_fp8_blocks(x, block_rows, signs=None):
     for idx in np.ndindex(*x.shape[:-2]):
         for b in range(nb):
             blk = x32[idx][b * block_rows:(b + 1) * block_rows]
-            s = pow2_block_scale(np.max(np.abs(blk)))
-            vals[idx][b * block_rows:(b + 1) * block_rows] = e4m3_round(np.clip(blk / s, -E4M3_MAX, E4M3_MAX))
+            s = fp8_block_scale(np.max(np.abs(blk)))
+            y = (blk / np.float32(s)).astype(np.float64)     # fp32 quotient
+            vals[idx][b * block_rows:(b + 1) * block_rows] = e4m3_round(np.clip(y, -E4M3_MAX, E4M3_MAX))
             scales[idx][b] = s
     return vals, scales
 
@@ -403,74 +401,87 @@ def _rows_of_blocks(scales, block_rows, N):
     return np.repeat(_f64(scales), block_rows, axis=-1)[..., :N]
 
 
-def ref_fwd_fp8(q8, k8, v8, sq, sk, sv, scale, causal=False, block_m=128, block_n=64, ref_shift=0,
-                tie_rel=None, score_rel=0.0):
-    """FP8 attention forward ([Triton-ch8] section 8.9.3): FP8 products with
-    fp32 (here exact) accumulation, the softmax statistics in high precision,
-    P~ quantised to FP8 before the second product.
+def ref_fwd_fp8(q8, k8, v8, sq, sk, sv, scale, causal=False, block_m=32, block_n=64, trace=False):
+    """FP8 attention forward, the method of [Triton-ch8] sections 8.9.3-8.9.4
+    and the fa3_fp8_inner listing of section 8.9.6, in fp64.
 
-    q8, k8, v8: [..., N, d] e4m3 values; sq: per-block Q scales
-    [..., ceil(N / block_m)]; sk, sv: per-block K and V scales
-    [..., ceil(N / block_n)] (dequantised value = e4m3 value x its block's
-    scale, section 8.9.4).  Per (b, h) and query row:
+    q8, k8, v8: [..., N, d] E4M3 values; sq: Q block scales [..., ceil(N /
+    block_m)]; sk, sv: K and V block scales [..., ceil(N / block_n)]
+    (dequantised value = E4M3 value x its block's scale).  Query rows are
+    processed in blocks of block_m (the listing's BLOCK_M), keys in blocks of
+    block_n (BLOCK_N), with the online state (m, l, acc) per row.  For each
+    (query block, key block) that holds a visible pair:
 
-        S   = scale (q8 sq) (k8 sk)^T        (masked if causal)
-        u   = S log2(e),   M = ceil(max_j u_j) + ref_shift   (an integer)
-        a_j = 2^(u_j - M + P_EXP),   l = sum_j a_j       (unquantised, as the
-                                                         page's fp32 l)
-        O   = sum_j e4m3(a_j) (v8_j sv_j) / l
-        LSE = (M + log2 l - P_EXP) ln 2
+        qk    = (q8 k8^T) sq sk scale               (masked to -inf if causal)
+        m_new = max(m, rowmax(qk)),   alpha = e^(m - m_new)
+        p     = e^(qk - m_new),       l = alpha l + rowsum(p)
+        scale_p = max(p) / 448        (over the whole block: all its rows
+                                       below N and all its keys)
+        p8    = e4m3(p / scale_p)     (P requantised to FP8)
+        acc   = alpha acc + (p8 v8) scale_p sv
 
-    P~ is thus quantised with the fixed scale 2^-P_EXP relative to an
-    integer reference instead of the page's data-dependent per-block p scale.
-    Since e4m3(a 2^k) = 2^k e4m3(a) while both are normal numbers, every
-    integer reference gives the same O up to values in the subnormal range;
-    ``ref_shift`` exists to pin that.  Returns (O [..., N, d], LSE [..., N]).
+    then O = acc / l and LSE = m + ln l.  The listing multiplies the whole
+    accumulator by scale_p scale_v after adding the block's product; that is
+    read as scaling the block's product only (the other reading mixes the
+    scales of different blocks).  p / scale_p is evaluated as
+    448 e^(qk - m_new - ln max(p)), which is the same number without the
+    underflow of a block whose p are all far below the running max (such a
+    block then adds scale_p ~ 0 times its product, as in fp32).  Blocks with
+    no visible pair are skipped (their p would all be 0).
 
-    With ``tie_rel`` = eps it also returns the rounding slack R [..., N, d]:
-    R_i = sum_j w_j |v_j| / l, where w_j is the gap between the E4M3
-    roundings of a_j's upper and lower error bounds (non-zero only when a tie
-    lies between them), plus one subnormal spacing 2^-9 for every
-    a_j < 2^-6.  The error bounds are a_j 2^(+-du_j) (1 +- eps), with
-    du_j = score_rel scale log2(e) max_d |q_d k_jd|: an implementation whose
-    scores are off by at most score_rel times their largest product, and
-    whose a_j carry a further relative error below eps, may round those a_j
-    the other way, or (with a reference M that leaves more a_j in the normal
-    range) round small a_j more finely; its l moves by at most a factor
-    2^Du (Du = max_j du_j + log2(1 + eps)).  Its O is then within
-    R = sum_j w_j |v_j| / l + |O| (2^Du - 1) of this one and its LSE within
-    RL = Du ln 2; with ``tie_rel`` the function returns (O, LSE, R, RL).
+    Returns (O [..., N, dv], LSE [..., N]).  With ``trace`` it also returns
+    Y, W [..., N, Nk]: Y the value each p8 was rounded from (p / scale_p;
+    NaN where a key is masked or its block skipped) and W the weight of one
+    unit of p8 in the final O, scale_p sv e^(m_new - m_final) / l_final, so
+    that O = sum_j e4m3(Y_ij) W_ij v8_j.
     """
     q8, k8, v8 = _f64(q8), _f64(k8), _f64(v8)
     N, Nk = q8.shape[-2], k8.shape[-2]
     O = np.zeros(q8.shape[:-1] + (v8.shape[-1],))
-    R = np.zeros(O.shape)
     LSE = np.full(q8.shape[:-1], NEG_INF)
-    RL = np.zeros(LSE.shape)
+    Y = np.full(q8.shape[:-1] + (Nk,), np.nan) if trace else None
+    W = np.zeros(q8.shape[:-1] + (Nk,)) if trace else None
     for h in _heads(q8.shape):
-        qd = q8[h] * _rows_of_blocks(sq[h], block_m, N)[:, None]
-        kd = k8[h] * _rows_of_blocks(sk[h], block_n, Nk)[:, None]
-        vd = v8[h] * _rows_of_blocks(sv[h], block_n, Nk)[:, None]
-        u = _scores(qd, kd, scale, causal, np.arange(N)) * np.log2(np.e)
-        for i in range(N):
-            vis = np.isfinite(u[i])
-            if not vis.any():
-                continue
-            M = np.ceil(np.max(u[i][vis])) + ref_shift
-            a = np.where(vis, np.exp2(np.where(vis, u[i], 0.0) - M + P_EXP), 0.0)
-            l = a.sum()
-            O[h][i] = (e4m3_round(a) @ vd) / l
-            LSE[h][i] = (M + np.log2(l) - P_EXP) * np.log(2.0)
-            if tie_rel is not None:
-                du = score_rel * abs(scale) * np.log2(np.e) * np.max(np.abs(qd[i][None, :] * kd), axis=1)
-                up = np.minimum(a * np.exp2(du) * (1 + tie_rel), E4M3_MAX)
-                w = e4m3_round(up) - e4m3_round(a * np.exp2(-du) * (1 - tie_rel))
-                w = w + np.where((a > 0) & (a < 2.0 ** -6), 2.0 ** -9, 0.0)
-                Du = np.max(np.where(vis, du, 0.0)) + np.log2(1 + tie_rel)
-                R[h][i] = (w @ np.abs(vd)) / l + np.abs(O[h][i]) * (2.0 ** Du - 1)
-                RL[h][i] = Du * np.log(2.0)
-    if tie_rel is not None:
-        return O, LSE, R, RL
+        sqr = _rows_of_blocks(sq[h], block_m, N)
+        for i0 in range(0, N, block_m):
+            i1 = min(i0 + block_m, N)
+            rows = np.arange(i0, i1)
+            m = np.full(i1 - i0, NEG_INF)
+            l = np.zeros(i1 - i0)
+            acc = np.zeros((i1 - i0, v8.shape[-1]))
+            blocks = []  # (key range, Y, unit weight before the final rescale, m_new)
+            for j0 in range(0, Nk, block_n):
+                j1 = min(j0 + block_n, Nk)
+                jb = j0 // block_n
+                qk = (q8[h][i0:i1] @ k8[h][j0:j1].T) * sqr[i0:i1, None] * float(sk[h][jb]) * scale
+                if causal:
+                    qk = np.where(np.arange(j0, j1)[None, :] > rows[:, None], NEG_INF, qk)
+                vis = np.isfinite(qk)
+                if not vis.any():
+                    continue
+                m_new = np.maximum(m, np.max(qk, axis=1))
+                alpha = np.where(np.isfinite(m), np.exp(m - np.where(np.isfinite(m_new), m_new, 0.0)), 0.0)
+                lp = np.where(vis, qk - np.where(np.isfinite(m_new), m_new, 0.0)[:, None], NEG_INF)  # ln p
+                p = np.exp(lp)
+                l = alpha * l + p.sum(axis=1)
+                lpmax = np.max(lp)                      # ln max(p), finite: the block has a visible pair
+                scale_p = np.exp(lpmax) / E4M3_MAX
+                y = np.where(vis, E4M3_MAX * np.exp(lp - lpmax), 0.0)   # p / scale_p, in [0, 448]
+                p8 = e4m3_round(y)
+                f = scale_p * float(sv[h][jb])
+                acc = alpha[:, None] * acc + (p8 @ v8[h][j0:j1]) * f
+                m = m_new
+                blocks.append((j0, j1, np.where(vis, y, np.nan), f, m_new.copy()))
+            has = l > 0
+            O[h][i0:i1] = np.where(has[:, None], acc / np.where(has, l, 1.0)[:, None], 0.0)
+            LSE[h][i0:i1] = np.where(has, m + np.log(np.where(has, l, 1.0)), NEG_INF)
+            if trace:
+                for j0, j1, y, f, mb in blocks:
+                    Y[h][i0:i1, j0:j1] = y
+                    w = f * np.exp(np.where(np.isfinite(mb), mb - m, 0.0)) / np.where(has, l, 1.0)
+                    W[h][i0:i1, j0:j1] = np.where(has & np.isfinite(mb), w, 0.0)[:, None]
+    if trace:
+        return O, LSE, Y, W
     return O, LSE
 
 

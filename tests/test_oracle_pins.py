@@ -465,35 +465,52 @@ def test_e4m3_round_values_from_the_format():
     assert ar.e4m3_round(np.array([-1.0625]))[0] == -1.0
 
 
-def test_pow2_block_scale():
-    for amax in (448.0, 449.0, 224.0, 224.5, 1.0, 3.5, 1e-3, 7e20):
-        s = ar.pow2_block_scale(amax)
-        assert math.log2(s) == int(math.log2(s))
-        assert 224.0 < amax / s <= 448.0, (amax, s)
-    assert ar.pow2_block_scale(0.0) == 1.0
-    assert ar.pow2_block_scale(1e-40) == 2.0 ** -126
+def _fp32_bits_value(sign_exp, frac_bits):
+    """An fp32 number written out from its fields: 2^sign_exp (1 + frac / 2^23)."""
+    return math.ldexp(1.0 + frac_bits / 2.0 ** 23, sign_exp)
+
+
+def test_fp8_block_scale_by_hand():
+    """scale = max|x| / 448 in fp32 ([Triton-ch8] section 8.9.4).  3 / 448 =
+    (12/7) 2^-8 and 12/7 = 1.101101101...b: the fraction's first 23 bits are
+    10110110110110110110110b with 110b following, so it rounds up to
+    ...110111b.  1 / 448 = 2^-9 (8/7) = 2^-9 1.001001001...b: the first 23
+    fraction bits are 00100100100100100100100b and 100b follows, so it
+    also rounds up."""
+    assert ar.fp8_block_scale(3.0) == _fp32_bits_value(-8, 0b10110110110110110110111)
+    assert ar.fp8_block_scale(1.0) == _fp32_bits_value(-9, 0b00100100100100100100101)
+    assert ar.fp8_block_scale(448.0) == 1.0 and ar.fp8_block_scale(3.5) == 2.0 ** -7
+    assert ar.fp8_block_scale(0.0) == 1.0
 
 
 def test_quantize_fp8_blocks_known_block():
-    x = np.array([[1.0, -2.0, 0.5], [0.25, 0.0, 1.5]])
+    """A block worked by hand: max|x| = 3, so x / scale is about 448 x / 3:
+    1 -> 149.33 (neighbours 144, 160: 144), -3 -> -448, 2 -> 298.67 (288,
+    320: 288), 0.5 -> 74.67 (72, 80: 72), 0 -> 0; none is near a midpoint,
+    so the fp32 rounding of the scale does not matter.  A second block of
+    row 2 alone has max 1.5 -> scale 1.5 / 448 and codes 448 and -149.33 ->
+    -144."""
+    x = np.array([[1.0, -3.0], [2.0, 0.5], [1.5, -0.5]])
     vals, scales = ar.quantize_fp8_blocks(x[None], 2)
-    # amax 2: 448 2^-8 = 1.75 < 2 <= 3.5 = 448 2^-7, so the scale is 2^-7
-    assert scales.tolist() == [[2.0 ** -7]]
-    assert vals[0].tolist() == [[128.0, -256.0, 64.0], [32.0, 0.0, 192.0]]
+    assert scales[0, 0] == ar.fp8_block_scale(3.0)
+    assert scales[0, 1] == _fp32_bits_value(-9, 0b10110110110110110110111)  # 1.5 / 448 = (12/7) 2^-9
+    assert vals[0].tolist() == [[144.0, -448.0], [288.0, 72.0], [448.0, -144.0]]
 
 
 def test_quantize_fp8_blocks_error_bound():
-    """Dequantised values are within half an e4m3 spacing of the input:
-    2^-4 relative in the normal range, 2^-10 x scale below it."""
+    """Dequantised values are within half an e4m3 spacing of the input
+    (2^-4 relative in the normal range, 2^-10 x scale below it, plus the
+    fp32 quotient's own rounding), and every full block reaches 448."""
     x = np.random.default_rng(61).standard_normal((2, 300, 64)) * np.exp2(np.arange(300) % 7)[:, None]
+    x = x.astype(np.float32).astype(np.float64)
     vals, scales = ar.quantize_fp8_blocks(x, 64)
     sr = np.repeat(scales, 64, axis=-1)[..., :300, None]
     deq = vals * sr
-    bound = np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * sr)
+    bound = np.maximum(2.0 ** -4 * np.abs(x), 2.0 ** -10 * sr) * (1 + 2.0 ** -20)
     assert np.all(np.abs(deq - x) <= bound)
     assert np.all(np.abs(vals) <= 448)
-    blk_max = np.abs(vals[:, :256]).reshape(2, 4, 64 * 64).max(-1)  # the four full blocks
-    assert np.all((blk_max >= 224) & (blk_max <= 448))
+    blk_max = np.abs(vals).reshape(2, -1)[:, :4 * 64 * 64].reshape(2, 4, -1).max(-1)
+    assert np.all(blk_max == 448)
 
 
 def test_hadamard_rotation_is_orthogonal():
@@ -510,7 +527,7 @@ def test_hadamard_rotation_is_orthogonal():
     assert np.allclose(np.abs(ar.hadamard_rotate(e, s)), 1.0 / 8.0)
 
 
-def _fp8_inputs(N, d, seed, bm=128, bn=64, scale_rows=None):
+def _fp8_inputs(N, d, seed, bm=32, bn=64, scale_rows=None):
     q, k, v = (_rand((1, 1, N, d), seed + i) for i in range(3))
     if scale_rows is not None:
         v = v * scale_rows[None, None, :, None]
@@ -526,7 +543,57 @@ def _dequant(x8, s, rows):
     return x8 * np.repeat(s, rows, axis=-1)[..., :x8.shape[-2], None]
 
 
+def test_fp8_forward_worked_by_hand():
+    """Four query rows in two blocks of two, four keys in two blocks of two,
+    d = 1, scale = ln 2 (so p = 2^(score in units of ln 2 - running max)).
+    K values k8 sk = [2, 1 | 3 x 0.5, -4 x 0.5] = [2, 1 | 1.5, -2], V values
+    v8 = [1, 2 | 4, 7] with sv = [1 | 2], queries q8 = [1, -1 | 1, 0.5].
+
+    Query block 0 (rows q = 1 and q = -1):
+      key block 0: scores [2, 1] and [-2, -1]: m = 2 and -1, p = [1, 1/2] and
+        [1/2, 1], max(p) = 1, so p / scale_p = 448 p = [448, 224], [224, 448]
+        (exact); acc = (448 v0 + 224 v1) / 448 = 2 and (224 + 896) / 448 = 2.5.
+      key block 1: scores [1.5, -2] (row 0: m stays 2, p = [2^-.5, 2^-4]) and
+        [-1.5, 2] (row 1: m -> 2, alpha = 2^-3, p = [2^-3.5, 1]); max(p) = 1;
+        448 p = [316.78 -> 320, 28] and [39.60 -> 40, 448];
+        acc0 = 2 + (320*4 + 28*7) * 2/448 = 2 + 369/56,
+        acc1 = 2.5/8 + (40*4 + 448*7) * 2/448 = 5/16 + 103/7.
+      l0 = 3/2 + 2^-.5 + 2^-4,  l1 = 3/2 / 8 + 2^-3.5 + 1.
+    Query block 1 (rows q = 1 and q = 0.5):
+      key block 0: row 2 as row 0; row 3 scores [1, .5]: m = 1, p = [1,
+        2^-.5]; max(p) = 1: 448 p = [448, 224] and [448, 316.78 -> 320];
+        acc2 = 2, acc3 = (448 + 640) / 448 = 17/7.
+      key block 1: row 2 p = [2^-.5, 2^-4]; row 3 scores [.75, -1], m stays 1,
+        p = [2^-.25, 2^-2].  Now max(p) = 2^-.25 (row 3), below 1, so
+        scale_p = 2^-.25 / 448 and p / scale_p = 448 p 2^.25:
+        row 2 [376.71 -> 384, 33.30 -> 32], row 3 [448, 133.19 -> 128];
+        acc2 += (384*4 + 32*7) * 2 * 2^-.25 / 448 = (55/7) 2^-.25,
+        acc3 += (448*4 + 128*7) * 2 * 2^-.25 / 448 = 12 * 2^-.25.
+      l2 = l0,  l3 = 1 + 2^-.5 + 2^-.25 + 1/4.
+    The roundings 320, 40, 384, 32 and 128 are each at least 1.2 from a
+    midpoint of their E4M3 neighbours.  LSE = (2, 2, 2, 1) ln 2 + ln l."""
+    q8 = np.array([1.0, -1.0, 1.0, 0.5]).reshape(1, 1, 4, 1)
+    k8 = np.array([2.0, 1.0, 3.0, -4.0]).reshape(1, 1, 4, 1)
+    v8 = np.array([1.0, 2.0, 4.0, 7.0]).reshape(1, 1, 4, 1)
+    sq, sk, sv = np.ones((1, 1, 2)), np.array([[[1.0, 0.5]]]), np.array([[[1.0, 2.0]]])
+    O, LSE, Y, W = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, math.log(2.0), block_m=2, block_n=2, trace=True)
+    r = 2.0 ** -0.5
+    q = 2.0 ** -0.25
+    want_codes = [[448, 224, 320, 28], [224, 448, 40, 448], [448, 224, 384, 32], [448, 320, 448, 128]]
+    assert ar.e4m3_round(Y[0, 0]).tolist() == want_codes
+    acc = [2 + 369 / 56, 5 / 16 + 103 / 7, 2 + 55 / 7 * q, 17 / 7 + 12 * q]
+    l = [1.5 + r + 1 / 16, 1.5 / 8 + r / 8 + 1, 1.5 + r + 1 / 16, 1 + r + q + 0.25]
+    m = [2, 2, 2, 1]
+    for i in range(4):
+        assert O[0, 0, i, 0] == pytest.approx(acc[i] / l[i], rel=1e-14), i
+        assert LSE[0, 0, i] == pytest.approx((m[i] + math.log2(l[i])) * math.log(2.0), rel=1e-14), i
+    # the trace reproduces O from the rounded values and their unit weights
+    np.testing.assert_allclose((ar.e4m3_round(Y[0, 0]) * W[0, 0]) @ v8[0, 0], O[0, 0], rtol=1e-14)
+
+
 def test_fp8_forward_uniform_scores_give_mean_of_v():
+    """Q = 0: every p is 1, p / scale_p = 448 exactly, so O is the mean of
+    the dequantised V and LSE = ln N."""
     N = 200
     q8, k8, v8, sq, sk, sv = _fp8_inputs(N, 64, 70)
     O, LSE = ar.ref_fwd_fp8(0 * q8, k8, v8, sq, sk, sv, 0.125)
@@ -535,91 +602,60 @@ def test_fp8_forward_uniform_scores_give_mean_of_v():
 
 
 def test_fp8_forward_single_key():
-    """One key: O = v^ e4m3(a) / a with a = 2^(u - ceil(u) + 3)."""
+    """One key: p = 1, p / scale_p = 448, O = the dequantised v, LSE = the
+    score."""
     q8, k8, v8, sq, sk, sv = _fp8_inputs(1, 64, 71)
-    u = 0.125 * float(_dequant(q8, sq, 128)[0, 0, 0] @ _dequant(k8, sk, 64)[0, 0, 0]) * math.log2(math.e)
-    a = 2.0 ** (u - math.ceil(u) + 3)
+    u = 0.125 * float(_dequant(q8, sq, 32)[0, 0, 0] @ _dequant(k8, sk, 64)[0, 0, 0])
     O, LSE = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125)
-    want = _dequant(v8, sv, 64)[0, 0, 0] * float(ar.e4m3_round(np.array([a]))[0]) / a
-    np.testing.assert_allclose(O[0, 0, 0], want, rtol=1e-13)
-    assert LSE[0, 0, 0] == pytest.approx(u * math.log(2), rel=1e-13)
+    np.testing.assert_allclose(O[0, 0, 0], _dequant(v8, sv, 64)[0, 0, 0], rtol=1e-14)
+    assert LSE[0, 0, 0] == pytest.approx(u, rel=1e-13)
 
 
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_forward_without_p_rounding_is_exact_attention(monkeypatch, causal):
-    """With P~ left unrounded the method is exact attention of the dequantised
-    inputs (section 8.9.4), so every step other than P~'s rounding is pinned
-    to the plain definition."""
-    q8, k8, v8, sq, sk, sv = _fp8_inputs(150, 64, 72, bm=32)
+@pytest.mark.parametrize("bm,bn", [(32, 64), (7, 13), (150, 150)])
+def test_fp8_forward_without_p_rounding_is_exact_attention(monkeypatch, causal, bm, bn):
+    """With P left unrounded the method is exact attention of the dequantised
+    inputs (section 8.9.3), for any block sizes, so every step other than
+    P's rounding (scales, the online max and alpha, scale_p and the V scale
+    of each block's product) is pinned to the plain definition."""
+    q8, k8, v8, sq, sk, sv = _fp8_inputs(150, 64, 72, bm=bm, bn=bn)
     monkeypatch.setattr(ar, "e4m3_round", lambda x: np.asarray(x, dtype=np.float64))
-    O, LSE = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125, causal, block_m=32)
-    O2, L2 = ar.ref_fwd(_dequant(q8, sq, 32), _dequant(k8, sk, 64), _dequant(v8, sv, 64), 0.125, causal)
+    O, LSE = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125, causal, block_m=bm, block_n=bn)
+    O2, L2 = ar.ref_fwd(_dequant(q8, sq, bm), _dequant(k8, sk, bn), _dequant(v8, sv, bn), 0.125, causal)
     np.testing.assert_allclose(O, O2, rtol=1e-12, atol=1e-13)
     np.testing.assert_allclose(LSE, L2, rtol=1e-13)
 
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_forward_error_within_p_rounding_bound(causal):
-    """O differs from exact attention of the dequantised inputs only by P~'s
-    rounding: |dO| <= sum_j |e4m3(a_j) - a_j| |v_j| / l <= (2^-4 + 2^-7) max|v|
-    (half a spacing: 2^-4 relative for normal a_j; subnormal a_j < 2^-6 are
-    off by at most 2^-10 each, and l >= 4 since M < max u + 1).  V's rows
-    vary in size so that a mix-up of V block scales breaks the bound."""
+    """O differs from exact attention of the dequantised inputs only by P's
+    rounding: every p8 / (p / scale_p) is within half an E4M3 spacing, 2^-4
+    relative (normal) or 2^-10 absolute (subnormal, with p / scale_p <= 448
+    and scale_p p-relative), so |dO| <= 2^-4 max|v| + N 2^-10 max|v| / 448.
+    V's rows vary in size so that a mix-up of V block scales breaks the
+    bound."""
     N = 256
     q8, k8, v8, sq, sk, sv = _fp8_inputs(N, 64, 73, scale_rows=np.exp2(np.arange(N) // 64 * 3.0))
     O, _ = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125, causal)
     vd = _dequant(v8, sv, 64)
-    O2, _ = ar.ref_fwd(_dequant(q8, sq, 128), _dequant(k8, sk, 64), vd, 0.125, causal)
+    O2, _ = ar.ref_fwd(_dequant(q8, sq, 32), _dequant(k8, sk, 64), vd, 0.125, causal)
     err = np.abs(O - O2)
-    assert err.max() <= (2.0 ** -4 + N * 2.0 ** -12) * np.abs(vd).max()
+    assert err.max() <= (2.0 ** -4 + N * 2.0 ** -10 / 448) * np.abs(vd).max()
     # and, on average, inside the per-key relative bound (errors of different keys partly cancel)
     assert np.sqrt((err ** 2).mean()) <= 2.0 ** -4 * np.sqrt((O2 ** 2).mean())
 
 
-def test_fp8_forward_integer_reference_shift():
-    """Every integer reference gives the same O while the a_j stay normal."""
-    q8, k8, v8, sq, sk, sv = _fp8_inputs(120, 64, 74)
-    O0, L0 = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.05)
-    for shift in (1, 2, -3):
-        O1, L1 = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.05, ref_shift=shift)
-        np.testing.assert_allclose(O1, O0, rtol=1e-13, atol=1e-15)
-        np.testing.assert_allclose(L1, L0, rtol=1e-13)
-
-
-def test_fp8_forward_rounding_slack():
-    """The slack bounds how far O moves when every a_j is perturbed by a
-    relative error below eps (as an fp32 evaluation would): the perturbed
-    results, computed by rounding perturbed a_j, stay within it; with eps = 0
-    and no subnormal a_j it is zero."""
-    q8, k8, v8, sq, sk, sv = _fp8_inputs(60, 64, 76)
-    eps = 2.0 ** -6  # large, so that the perturbations below do flip roundings
-    O, _, R, _ = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125, tie_rel=eps)
-    flipped = False
-    rng = np.random.default_rng(77)
-    true_round = ar.e4m3_round
-    for _ in range(3):
-        delta = rng.uniform(-eps, eps, 60)
-
-        def jittered(x, _d=delta):
-            x = np.asarray(x, dtype=np.float64)
-            return true_round(np.minimum(x * (1 + _d[:x.shape[-1]]), 448.0)) if x.ndim == 1 and x.shape[0] == 60 \
-                else true_round(x)
-
-        ar.e4m3_round = jittered
-        try:
-            Oj, _ = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125)
-        finally:
-            ar.e4m3_round = true_round
-        assert np.all(np.abs(Oj - O) <= R + 1e-15)
-        flipped |= bool(np.any(Oj != O))
-    assert flipped
-    # uniform scores: every a_j is exactly 8, far from a tie and normal
-    O0, _, R0, RL0 = ar.ref_fwd_fp8(0 * q8, k8, v8, sq, sk, sv, 0.125, tie_rel=eps)
-    np.testing.assert_allclose(R0, np.abs(O0) * eps, rtol=1e-6)   # only l's own error remains
-    np.testing.assert_allclose(RL0, np.log1p(eps), rtol=1e-12)
-    # a score error bound widens every band, so the slack can only grow
-    _, _, R1, RL1 = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125, tie_rel=eps, score_rel=2.0 ** -9)
-    assert np.all(R1 >= R) and np.any(R1 > R) and np.all(RL1 > RL0[..., :1])
+def test_fp8_forward_block_max_spans_the_rows():
+    """The P scale is one per block of rows and keys: a row whose own largest
+    p in a key block is below the block's largest p is rounded on a finer
+    relative grid than alone.  Splitting the same inputs into one-row blocks
+    changes those rows' results, and only by P rounding."""
+    q8, k8, v8, sq, sk, sv = _fp8_inputs(256, 64, 78)
+    O32, _ = ar.ref_fwd_fp8(q8, k8, v8, sq, sk, sv, 0.125, block_m=32)
+    sq1 = np.repeat(sq, 32, axis=-1)
+    O1, _ = ar.ref_fwd_fp8(q8, k8, v8, sq1, sk, sv, 0.125, block_m=1)
+    assert np.any(O1 != O32)
+    np.testing.assert_allclose(O1, O32, atol=2.0 ** -3 * np.abs(_dequant(v8, sv, 64)).max())
 
 
 def test_hadamard_rotation_helps_outlier_features():
@@ -788,6 +824,26 @@ def test_mutant_fp8_v_scale_mixup_fails_bound(monkeypatch):
     monkeypatch.setattr(ar, "_rows_of_blocks", bad_rows)
     with pytest.raises(AssertionError):
         test_fp8_forward_error_within_p_rounding_bound(False)
+
+
+@pytest.mark.parametrize("orig,mutated", [
+    # the listing's last line taken literally: the whole accumulator times scale_p sv after each block
+    ("acc = alpha[:, None] * acc + (p8 @ v8[h][j0:j1]) * f", "acc = (alpha[:, None] * acc + p8 @ v8[h][j0:j1]) * f"),
+    # a P scale per row instead of one over the block's rows and keys
+    ("lpmax = np.max(lp)", "lpmax = np.max(lp, axis=1, keepdims=True)"),
+    # the block's product without its V scale
+    ("f = scale_p * float(sv[h][jb])", "f = scale_p"),
+])
+def test_mutant_fp8_forward_fails_hand_worked_block(monkeypatch, orig, mutated):
+    """Plausible misreadings of the FP8 method must break the hand-worked pin
+    (a per-row P scale changes the trace's shapes, so it may fail there)."""
+    src = open(ar.__file__).read()
+    assert src.count(orig) == 1
+    ns = {"__name__": "mutant"}
+    exec(compile(src.replace(orig, mutated), ar.__file__, "exec"), ns)
+    monkeypatch.setattr(ar, "ref_fwd_fp8", ns["ref_fwd_fp8"])
+    with pytest.raises((AssertionError, ValueError)):
+        test_fp8_forward_worked_by_hand()
 
 
 def test_mutant_lse_merge_without_weights_fails_union_pin(monkeypatch):
