@@ -17,7 +17,7 @@ inputs:
     kernel per shard, and the fused steps replayed as one captured HIP graph
     (reported only)
   * forward on FP8 (E4M3) storage of the headline Q, K, V (per-block
-    power-of-two scales: Q per 128 rows, K and V per 64; quantised before the
+    max|x| / 448 scales: Q per 32 rows, K and V per 64; quantised before the
     timed region), non-causal (reported only)
   * the same backward with dQ accumulated by fp32 atomic adds in the dK/dV
     pass (zero fill + preprocess + dK/dV/dQ + dQ scaling; reported only)
@@ -48,7 +48,7 @@ FWD_LONG = dict(B=2, H=32, N=8192, d=128, causal=True, input_scale=0.5)
 DEC = dict(B=16, H=32, L=32768, d=128, S=256)
 DEC_PAGED = dict(DEC, block_size=16)
 BWD = dict(B=2, H=16, N=4096, d=64, causal=True)
-FP8_BLOCKS = (128, 64)  # rows per scale: Q, then K and V
+FP8_BLOCKS = (32, 64)  # rows per scale: Q, then K and V (the forward's BLOCK_M and BLOCK_N)
 RING_G = 8  # GPUs in the ring whose per-GPU share is timed
 
 

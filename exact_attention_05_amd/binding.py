@@ -290,8 +290,8 @@ def _check_fp8(name, t, shape, device):
 
 
 def attn_quantize_fp8(x, block_rows, signs=None, out=None, scales=None):
-    """Block quantisation of bf16 x [B, H, N, d] to E4M3 bytes plus one
-    power-of-two fp32 scale per block of ``block_rows`` rows, optionally after
+    """Block quantisation of bf16 x [B, H, N, d] to E4M3 bytes plus one fp32
+    scale (max|x| / 448) per block of ``block_rows`` rows, optionally after
     the Hadamard rotation with ``signs`` (d floats of +-1).
 
     Returns (x8 uint8 [B, H, N, d], scales fp32 [B, H, ceil(N / block_rows)]).
@@ -316,11 +316,12 @@ def attn_quantize_fp8(x, block_rows, signs=None, out=None, scales=None):
     return out, scales
 
 
-def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, block_m, block_n, scale=None, causal=False, out=None,
+def attn_fwd_fp8(q8, k8, v8, q_scale, k_scale, v_scale, block_m=32, block_n=64, scale=None, causal=False, out=None,
                  lse=None):
     """Attention forward on E4M3 inputs [B, H, N, d] (uint8 bit patterns)
-    with power-of-two per-block scales (q_scale [B, H, ceil(N / block_m)],
-    k_scale and v_scale [B, H, ceil(N / block_n)]).
+    with positive fp32 per-block scales (q_scale [B, H, ceil(N / block_m)],
+    k_scale and v_scale [B, H, ceil(N / block_n)]); the library supports
+    block_m = 32 and block_n = 64.
 
     Returns (o bf16 [B, H, N, d], lse fp32 [B, H, N]).
     """

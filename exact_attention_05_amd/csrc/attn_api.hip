@@ -163,14 +163,13 @@ attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const f
                          int block_n, float scale, int causal, void* stream) {
   attn_status st = check_common(B, H, N, d, ATTN_BF16, scale);
   if (st != ATTN_OK) return st;
-  if (block_m < 32 || block_m % 32 != 0 || block_n < 64 || block_n % 64 != 0) return ATTN_ERR_INVALID_ARG;
+  if (block_m < 1 || block_n < 1) return ATTN_ERR_INVALID_ARG;
   if (!tensor_ok(q8) || !tensor_ok(k8) || !tensor_ok(v8) || !tensor_ok(o)) return ATTN_ERR_INVALID_ARG;
   for (const float* p : {q_scale, k_scale, v_scale})
     if (p == nullptr || !aligned(p, 4)) return ATTN_ERR_INVALID_ARG;
   if (lse != nullptr && !aligned(lse, 4)) return ATTN_ERR_INVALID_ARG;
-  if (d != 64) return ATTN_ERR_UNSUPPORTED;
-  attn::Fp8FwdArgs a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, block_m, block_n, scale,
-                     causal != 0};
+  if (d != 64 || block_m != 32 || block_n != 64) return ATTN_ERR_UNSUPPORTED;
+  attn::Fp8FwdArgs a{q8, k8, v8, q_scale, k_scale, v_scale, o, lse, B, H, N, d, scale, causal != 0};
   return from_hip(attn::launch_fwd_fp8(a, static_cast<hipStream_t>(stream)));
 }
 

@@ -1,35 +1,36 @@
 // FP8 (E4M3) attention forward and block quantisation for gfx950
 // ("8. FlashAttention 实战", triton-tutorial.pages.dev, section 8.9).
 //
-// Storage: Q, K, V in E4M3 with one scale per block of rows (section 8.9.4).
-// The scales are powers of two, so the matrix unit applies them:
-// v_mfma_scale_f32_32x32x64_f8f6f4 takes an E8M0 exponent per row of A and
-// per column of B (for each 32-wide half of the reduction), which is the
-// exponent field of the fp32 scale.  Dequantisation therefore costs nothing.
+// Storage: Q, K, V in E4M3 with one fp32 scale per block of rows, the page's
+// max|x| / 448 (section 8.9.4): Q per 32 rows (BLOCK_M), K and V per 64
+// (BLOCK_N).  The quantiser below writes both.
 //
-// Forward (d = 64), the scheme of the bf16 d = 64 kernel in fwd.hip: 16
-// wavefronts of 32 query rows, four per SIMD in two groups one phase apart,
-// 64-key K/V tiles copied HBM -> LDS ahead of use.  Per tile and wavefront:
-//   S^T = K Q^T   two MFMAs (keys 0-31, 32-63), reduction over d = 64 in one
-//                 instruction; scale_a = the K block's exponent, scale_b = the
-//                 query row's Q block exponent;
-//   P~ = 2^(s log2(e) scale - M + 3), M an integer reference per row, summed
-//                 unrounded into l and rounded to E4M3 for the next product
-//                 (section 8.9.3: softmax statistics in high precision, P
-//                 requantised to FP8);
-//   O^T += V^T P~^T  two MFMAs (d rows 0-31, 32-63), reduction over the 64
-//                 keys; scale_a = the V block's exponent.
-// P~ goes from the score accumulator straight into the B operand (a lane
-// holds 32 keys of its query); the V^T operand is read with transposing
-// 8-bit LDS reads whose source rows follow the same key order.
-//
-// Reference M: the ceiling of the row max of the first tile (key 0 is visible
-// to every row).  P~ <= 2^3 while no score exceeds M; a lane checks that the
-// sum of its 32 P~ stays <= 448 (so no single value can exceed the largest
-// E4M3 number), and otherwise the wavefront moves M to the ceiling of the
-// running max, rescales U and l by the exact power of two 2^(M_old - M_new)
-// and redoes the tile.  Because M is an integer, E4M3 rounding of P~ does not
-// depend on which reference is used (up to values in the subnormal range).
+// Forward (d = 64), the method of section 8.9.3 and the listing of section
+// 8.9.6 with BLOCK_M = 32 query rows (one wavefront) and BLOCK_N = 64 keys
+// (one K/V tile).  Eight wavefronts of 32 query rows per workgroup, two
+// workgroups per CU (four wavefronts per SIMD), the wavefronts of a workgroup
+// in two groups one phase apart as in the bf16 d = 64 kernel, 64-key tiles
+// copied HBM -> LDS ahead of use.
+// Per tile j and wavefront:
+//   S^T = K8 Q8^T     two FP8 MFMAs (keys 0-31, 32-63), the whole d = 64
+//                     reduction in one instruction each;
+//   u = S sq sk_j scale log2(e)          (scores in base-2 units; masked)
+//   m_new = max(m, rowmax u), alpha = 2^(m - m_new)       (per query row)
+//   e = max over the block's rows of (rowmax u - m_new)    (wave-wide):
+//                     the block's largest p = 2^(u - m_new) is 2^e, so
+//                     scale_p = 2^e / 448 and p / scale_p = 2^(u - m_new - e) 448
+//   P8 = e4m3(p / scale_p)   (the probabilities requantised to FP8)
+//   l = alpha l + 2^e / 448 * sum(p / scale_p)   (p unrounded, as the page's l)
+//   T = V8^T P8^T     two FP8 MFMAs in the next matrix phase, and there
+//   U = alpha U + (scale_p sv_j) T            (the block's product scaled by
+//                     its own scales; the listing scales the whole accumulator)
+//                     before the next tile's score products, so T and S are
+//                     never live together (no register spills at 128 VGPRs)
+// and at the end O = U / l, LSE = (m + log2 l) ln 2.  Rows past N do not take
+// part in the block's max.  P8 goes from the score accumulator straight into
+// the B operand (a lane holds 32 keys of its query); the V^T operand is read
+// with transposing 8-bit LDS reads whose source rows follow the same key
+// order.
 #include "common.h"
 #include "launch.h"
 
@@ -39,18 +40,15 @@ namespace {
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kFp8Bc = 64;        // keys per tile
+constexpr int kFp8Bc = 64;        // keys per tile (BLOCK_N)
 constexpr int kFp8Row = 64;       // bytes per row (d = 64, one byte each)
 constexpr int kFp8Tile = 64 * 64; // bytes per K or V tile
 constexpr float kP8Max = 448.f;   // largest finite E4M3 value
-constexpr float kPExp = 3.f;      // P~ = 2^(u - M + kPExp)
+constexpr float kLog2P8Max = 8.807354922057604f;  // log2(448)
 constexpr int kE8One = 127;       // E8M0 encoding of 1.0
 
-// E8M0 exponent of a power-of-two fp32 scale: its biased exponent field.
-__device__ __forceinline__ int e8m0_of(float s) { return (__float_as_uint(s) >> 23) & 0xFF; }
-
-__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c, int sa, int sb) {
-  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+__device__ __forceinline__ f32x16 mfma_fp8(const i32x8& a, const i32x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, kE8One, 0, kE8One);
 }
 
 // Transposing LDS read of 8-bit values (ds_read_b64_tr_b8).  Within every
@@ -66,22 +64,43 @@ __device__ __forceinline__ i32x2 lds_read_tr8(const void* lds_addr) {
 // {k0..k0+3, k0+8..k0+11} x 4 chunk-halves (ds_read_b64_tr_b8, 32 lanes).
 __device__ __forceinline__ int fp8_off(int k, int c) { return 64 * k + 16 * (c ^ ((k >> 2) & 3)); }
 
-// Key of byte J of a lane in half h of the P~ operand: the score
+// Key of byte J of a lane in half h of the P8 operand: the score
 // accumulator's row order (block J / 16, accumulator index J % 16).
 __device__ __forceinline__ constexpr int pkey(int h, int J) { return 32 * (J >> 4) + acc_row(J & 15, h); }
 
+// v_permlane32_swap of x with itself: the first result holds x of lanes
+// 0-31 in both halves of the wave, the second x of lanes 32-63; a symmetric
+// combination of the two is the lane pair's (l, l ^ 32) value in every lane.
+__device__ __forceinline__ float max_of_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_of_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Max of `x` over lanes 0-31 (lanes 32-63 hold the same values), wave-uniform.
+__device__ __forceinline__ float max_over_32_lanes(float x) {
+  x = fmaxf(x, __builtin_amdgcn_update_dpp(kNegInf, x, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+  x = fmaxf(x, __builtin_amdgcn_update_dpp(kNegInf, x, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+  x = fmaxf(x, __builtin_amdgcn_update_dpp(kNegInf, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  x = fmaxf(x, __builtin_amdgcn_update_dpp(kNegInf, x, 0x140, 0xF, 0xF, false));  // row_mirror
+  return fmaxf(__uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 0)),
+               __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 16)));
+}
+
 // ---------------------------------------------------------------------------
 // Forward kernel, d = 64.  Work ids, eight wavefronts (256 query rows) per
-// workgroup and two workgroups per CU, ring of five tiles, phase structure
-// and barriers as fwd_pp4_kernel; waves 0-3 copy the K tile and 4-7 the V
-// tile.
+// workgroup, two workgroups per CU, ring of five tiles, phase structure and
+// barriers as fwd_pp4_kernel.  Every wavefront copies 1 KB of the K tile or
+// the V tile.
 // ---------------------------------------------------------------------------
 template <bool CAUSAL>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void fwd_fp8_kernel(
     const uint8_t* __restrict__ Q, const uint8_t* __restrict__ K, const uint8_t* __restrict__ V,
     const float* __restrict__ QS, const float* __restrict__ KS, const float* __restrict__ VS,
-    __bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg, int block_m,
-    int block_n, float scale_log2) {
+    __bf16* __restrict__ O, float* __restrict__ LSE, int N, int n_qtiles, int total_wg, float scale_log2) {
   constexpr int D = 64;
   constexpr int NW = 8;
   constexpr int BR = NW * 32;
@@ -108,23 +127,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int qr = qw0 + l32;
   const int kend = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kend + kFp8Bc - 1) / kFp8Bc;
-  const int nkb = (N + block_n - 1) / block_n;
+  const int nkb = (N + kFp8Bc - 1) / kFp8Bc;
   const float* ksh = KS + (int64_t)bh * nkb;
   const float* vsh = VS + (int64_t)bh * nkb;
 
   // copy geometry: waves 0-3 fill the K tile, 4-7 the V tile, 1 KB each;
   // lane l fills physical chunk l % 4 of row 16 (wave % 4) + l / 4.
-  const bool copier = wave < 8;  // every wavefront of the workgroup
   const uint8_t* csrc = (wave < 4 ? K : V) + base;  // wave-uniform
   const int crow = 16 * (wave & 3) + (lane >> 2);
   const int ccol = 16 * ((lane & 3) ^ ((crow >> 2) & 3));
   const int cdst = (wave < 4 ? 0 : kFp8Tile) + 1024 * (wave & 3);
   auto issue_tile = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
-    if (copier) {
-      // rows past N read row N-1 (masked later); a head spans < 2^31 bytes
-      const uint32_t off = (uint32_t)(min(j * kFp8Bc + crow, N - 1) * kFp8Row + ccol);
-      global_to_lds16(csrc + off, buf + cdst);
-    }
+    // rows past N read row N-1 (masked later); a head spans < 2^31 bytes
+    const uint32_t off = (uint32_t)(min(j * kFp8Bc + crow, N - 1) * kFp8Row + ccol);
+    global_to_lds16(csrc + off, buf + cdst);
   };
 
   issue_tile(0, sb0);
@@ -138,9 +154,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const u32x4 a = qp[0], b = qp[1];
     qB = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
   }
-  // block_m is a multiple of 32, so the wavefront's rows share one Q scale
-  const int qexp =
-      __builtin_amdgcn_readfirstlane(e8m0_of(QS[(int64_t)bh * ((N + block_m - 1) / block_m) + min(qw0, N - 1) / block_m]));
+  // the wavefront's 32 rows are one Q scale block
+  const float cq = scale_log2 * QS[(int64_t)bh * ((N + 31) / 32) + min(qw0, N - 1) / 32];
 
   // Per-lane LDS offsets.  K rows (S operand): chunks 2g and 2g+1 of row
   // l32; rows 32 further (the second key half) share the swizzle phase, +2048.
@@ -156,11 +171,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   }
 
   f32x16 oacc[2] = {f32x16{}, f32x16{}};
-  float M = kNegInf, lsum = 0.f, rs = 0.f;
+  f32x16 tacc[2];  // T = V8^T P8^T of the previous tile
+  float m = kNegInf, lsum = 0.f;
+  float alpha_prev = 1.f, f_prev = 0.f;  // the previous tile's alpha (per row) and scale_p sv (per wavefront)
   f32x16 sacc[2];
-  i32x8 pb;  // P~ of the current tile as E4M3, the B operand of O^T += V^T P~^T
-  int kexp = e8m0_of(ksh[0]);
-  int vexp = kexp, vexp_prev = kexp;
+  i32x8 pb;  // P8 of the current tile, the B operand of T
+  float ck = cq * ksh[0];
 
   // MFMA operands, all read from LDS at the top of the matrix phase so that
   // their latencies overlap (V^T of the previous tile, K of this one).
@@ -183,31 +199,44 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       va[mt] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
     }
   };
-  auto scores = [&](int ke) __attribute__((always_inline)) {
+  // U = alpha U + f T for the previous tile's product
+  auto accumulate = [&]() __attribute__((always_inline)) {
+    if (__builtin_expect(__ballot(alpha_prev != 1.f) != 0, 0)) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) sacc[hb] = mfma_fp8(ka[hb], qB, f32x16{}, ke, qexp);
+      for (int mt = 0; mt < 2; ++mt) oacc[mt] *= alpha_prev;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) oacc[mt][i] = fmaf(tacc[mt][i], f_prev, oacc[mt][i]);
   };
-  // M: O^T += V^T P~^T of the previous tile, then S^T of this one, from the
-  // operands read at the end of the previous vector phase.
-  // `copy` runs after the operand reads: a tile copy issued before them makes
-  // the compiler wait for it (it cannot always tell the buffers apart).
+
+  // M: T = V^T P8^T of the previous tile, added into U with that tile's
+  // alpha and scales, then S^T of this one; the K operands are read after the
+  // addition so that T and S are never live together.  `copy` runs after the
+  // V operand reads: a tile copy issued before them makes the compiler wait
+  // for it (it cannot always tell the buffers apart).
   auto mph = [&](const unsigned char* kt, const unsigned char* vt, const bool do_pv, const bool do_s,
                  auto&& copy) __attribute__((always_inline)) {
     if (do_pv) read_v(vt + kFp8Tile);
-    if (do_s) read_k(kt);
     copy();
     __builtin_amdgcn_s_setprio(1);
     if (do_pv) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) oacc[mt] = mfma_fp8(va[mt], pb, oacc[mt], vexp_prev, kE8One);
+      for (int mt = 0; mt < 2; ++mt) tacc[mt] = mfma_fp8(va[mt], pb, f32x16{});
+      __builtin_amdgcn_sched_barrier(0);
+      accumulate();
+      asm volatile("" : "+v"(oacc[0]), "+v"(oacc[1])::"memory");
     }
-    if (do_s) scores(kexp);
+    if (do_s) read_k(kt);
+    if (do_s) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) sacc[hb] = mfma_fp8(ka[hb], qB, f32x16{});
+    }
     // keep the products in this phase (the barrier after it orders memory only)
-    if (do_pv) asm volatile("" : "+v"(oacc[0]), "+v"(oacc[1]));
     if (do_s) asm volatile("" : "+v"(sacc[0]), "+v"(sacc[1]));
     __builtin_amdgcn_s_setprio(0);
   };
-
   auto mask_tile = [&](int j) __attribute__((always_inline)) {
     const int kb = j * kFp8Bc;
     if ((kb + kFp8Bc > N) || (CAUSAL && kb + kFp8Bc - 1 > qw0)) {
@@ -221,62 +250,40 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
         }
     }
   };
-  auto row_max_ceil = [&]() __attribute__((always_inline)) {
+  // V(j): the previous tile's product into U, then the online softmax of tile j.
+  auto vph = [&](int j) __attribute__((always_inline)) {
+    mask_tile(j);
+    // row max of the raw scores (the block's scales are positive)
     float mx = kNegInf;
 #pragma unroll
     for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[1][i]));
-    mx = fmaxf(mx, shfl_xor_f32(mx, 32));
-    return ceilf(mx * scale_log2);
-  };
-  // P~ = 2^(s c - M + 3) in E4M3 (byte J of the lane = key pkey(g, J)); rs = fp32 sum
-  auto expo = [&]() __attribute__((always_inline)) {
-    const float off = kPExp - M;
+    mx = max_of_halves(mx);
+    const float bm = mx * ck;  // the row's largest u in this block (-inf: none visible)
+    const float m_new = fmaxf(m, bm);
+    const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m - m_new);
+    // e = log2 of the block's largest p, over its rows below N
+    const float e = max_over_32_lanes(qr < N ? bm - m_new : kNegInf);
+    const float off = e == kNegInf ? 0.f : m_new + e - kLog2P8Max;
     float r4[4];
 #pragma unroll
     for (int w = 0; w < 8; ++w) {
       float x[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[e] = fast_exp2(fmaf(sacc[w >> 2][4 * (w & 3) + e], scale_log2, off));
+      for (int q = 0; q < 4; ++q) x[q] = fast_exp2(fmaf(sacc[w >> 2][4 * (w & 3) + q], ck, -off));
       if ((w & 1) == 0) r4[w >> 1] = (x[0] + x[1]) + (x[2] + x[3]);
       else r4[w >> 1] += (x[0] + x[1]) + (x[2] + x[3]);
       const int pw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
       pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], pw, true);
     }
-    rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
-  };
-  // V(j): tile j is at cur (its K is read again only by the rare rescue).
-  auto vph = [&](int j, const unsigned char* cur) __attribute__((always_inline)) {
-    mask_tile(j);
-    if (j == 0) M = row_max_ceil();
-    expo();
-    if (__builtin_expect(__ballot(!(rs <= kP8Max)) != 0, 0)) {
-      // rare: a P~ could exceed the E4M3 range; move the reference up and redo the tile
-      __builtin_amdgcn_sched_barrier(0);
-      read_k(cur);
-      scores(kexp);
-      mask_tile(j);
-      const float mn = fmaxf(M, row_max_ceil());
-      const float alpha = fast_exp2(M - mn);  // an exact power of two
-      M = mn;
-      lsum *= alpha;
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) oacc[mt] *= alpha;
-      expo();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    lsum += rs;
+    const float rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
+    const float sp = fast_exp2(e) * (1.f / kP8Max);  // scale_p (0 for an empty block)
+    lsum = fmaf(rs, sp, lsum * alpha);
+    m = m_new;
+    alpha_prev = alpha;
+    f_prev = sp * vsh[j];
+    if (j + 1 < ntiles) ck = cq * ksh[j + 1];
     asm volatile("" : "+v"(pb));
   };
-  // scale exponents of tile j+1, read while tile j is processed
-  auto next_scales = [&](int j) __attribute__((always_inline)) {
-    vexp_prev = vexp;
-    if (j + 1 < ntiles) {
-      const int kb = ((j + 1) * kFp8Bc) / block_n;
-      kexp = e8m0_of(ksh[kb]);
-      vexp = e8m0_of(vsh[kb]);
-    }
-  };
-  vexp = e8m0_of(vsh[0]);
 
   if (ntiles > 2) wait_vm_at_most<2>(); else if (ntiles > 1) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
   lds_barrier();
@@ -284,8 +291,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   mph(sb0, sb0, false, true, [&]() __attribute__((always_inline)) { if (ntiles > 3) issue_tile(3, sb3); });
   if (ntiles > 3) wait_vm_at_most<2>(); else if (ntiles > 2) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
   lds_barrier();
-  vph(0, sb0);
-  next_scales(0);
+  vph(0);
   // Tile j at cur, j-1 at prev; tile j+3 goes to far (the slot of j-2).
   auto step = [&](int j, const unsigned char* cur, const unsigned char* prev, unsigned char* far)
       __attribute__((always_inline)) {
@@ -293,8 +299,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     mph(cur, prev, true, true, [&]() __attribute__((always_inline)) { if (j + 3 < ntiles) issue_tile(j + 3, far); });
     if (j + 3 < ntiles) wait_vm_at_most<2>(); else if (j + 2 < ntiles) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
     lds_barrier();
-    vph(j, cur);
-    next_scales(j);
+    vph(j);
   };
   for (int j = 1; j < ntiles; j += 5) {
     step(j, sb1, sb0, sb4);
@@ -311,7 +316,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   }
   if (lead) lds_barrier();
 
-  const float lt = lsum + shfl_xor_f32(lsum, 32);
+  const float lt = sum_of_halves(lsum);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   if (qr < N) {
     __bf16* Oh = O + base;
@@ -324,22 +329,22 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                    pack_bf16x2(oacc[mt][4 * c + 2] * inv, oacc[mt][4 * c + 3] * inv)};
         *reinterpret_cast<u32x2*>(Oh + (int64_t)qr * D + d0) = w;
       }
-    if (g == 0 && LSE != nullptr)
-      LSE[(int64_t)bh * N + qr] = lt > 0.f ? (M + fast_log2(lt) - kPExp) * kLn2 : kNegInf;
+    if (g == 0 && LSE != nullptr) LSE[(int64_t)bh * N + qr] = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : kNegInf;
   }
 }
 
 // ---------------------------------------------------------------------------
-// Block quantisation: one workgroup per block of rows of one (b, h).  Each
-// thread holds 8 consecutive values of a row (D / 8 threads per row).  With
-// signs, each row is first rotated, y = (x o signs) H / sqrt(D) (fast
-// Walsh-Hadamard transform: three butterfly stages inside the thread, the
-// rest across the row's lanes).  Pass 1 takes max|y| over the block; the
-// scale is 2^k, the smallest power of two with 448 2^k >= max|y| (k >= -126,
-// 1 for a zero block); pass 2 writes e4m3(y 2^-k), rounded to nearest even.
-// When the block spans at most NP passes of rows, its values stay in
-// registers after one read (all loads issued before any is used); NP = 0
-// reads the block twice.
+// Block quantisation ("8. FlashAttention 实战", section 8.9.4): one workgroup
+// per block of rows of one (b, h).  Each thread holds 8 consecutive values of
+// a row (D / 8 threads per row).  With signs, each row is first rotated,
+// y = (x o signs) H / sqrt(D) (section 8.9.5; fast Walsh-Hadamard transform:
+// three butterfly stages inside the thread, the rest across the row's lanes).
+// Pass 1 takes max|y| over the block; the scale is max|y| / 448 (1 for an
+// all-zero block), an IEEE fp32 division as in the page's tensor code; pass 2
+// writes e4m3(clamp(y / scale, +-448)), y / scale again divided in fp32 and
+// rounded to nearest even.  When the block spans at most NP passes of rows,
+// its values stay in registers after one read (all loads issued before any
+// is used); NP = 0 reads the block twice.
 // ---------------------------------------------------------------------------
 template <int D, bool ROT, int NP>
 __global__ __launch_bounds__(256) void quant_fp8_kernel(const __bf16* __restrict__ X, const float* __restrict__ signs,
@@ -432,15 +437,8 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const __bf16* __restrict
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 
-  // k: smallest integer with 448 2^k >= amax (448 = 1.75 2^8), clamped to >= -126
-  int k = 0;
-  if (amax > 0.f) {
-    const uint32_t bits = __float_as_uint(amax);
-    const int e = (int)((bits >> 23) & 0xFF) - 127;
-    k = ((bits >> 23) & 0xFF) == 0 ? -126 : ((bits & 0x7FFFFF) <= 0x600000u ? e - 8 : e - 7);
-    k = max(k, -126);
-  }
-  if (tid == 0) scales[(int64_t)bh * nblk + b] = ldexpf(1.f, k);
+  const float scale = amax > 0.f ? __fdiv_rn(amax, kP8Max) : 1.f;
+  if (tid == 0) scales[(int64_t)bh * nblk + b] = scale;
 
   // pass 2: codes
   uint8_t* X8h = X8 + (int64_t)bh * N * D;
@@ -450,7 +448,7 @@ __global__ __launch_bounds__(256) void quant_fp8_kernel(const __bf16* __restrict
     for (int h = 0; h < 2; ++h) {
       float z[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) z[e] = fminf(fmaxf(ldexpf(y[4 * h + e], -k), -kP8Max), kP8Max);
+      for (int e = 0; e < 4; ++e) z[e] = fminf(fmaxf(__fdiv_rn(y[4 * h + e], scale), -kP8Max), kP8Max);
       int pw = __builtin_amdgcn_cvt_pk_fp8_f32(z[0], z[1], 0, false);
       w[h] = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(z[2], z[3], pw, true);
     }
@@ -480,8 +478,7 @@ hipError_t run_fp8(const Fp8FwdArgs& a, hipStream_t s) {
   const int total = n_qtiles * a.B * a.H;
   hipLaunchKernelGGL((fwd_fp8_kernel<CAUSAL>), dim3(total), dim3(512), 0, s, static_cast<const uint8_t*>(a.q),
                      static_cast<const uint8_t*>(a.k), static_cast<const uint8_t*>(a.v), a.q_scale, a.k_scale,
-                     a.v_scale, static_cast<__bf16*>(a.o), a.lse, a.N, n_qtiles, total, a.block_m, a.block_n,
-                     a.scale * kLog2e);
+                     a.v_scale, static_cast<__bf16*>(a.o), a.lse, a.N, n_qtiles, total, a.scale * kLog2e);
   return hipGetLastError();
 }
 

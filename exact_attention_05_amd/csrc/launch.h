@@ -51,8 +51,8 @@ hipError_t launch_decode_paged_bf16(const DecodeArgs& a, const PagedArgs& p, hip
 constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
 hipError_t launch_decode_noalloc_bf16(const DecodeArgs& a, hipStream_t s);
 
-// FP8 forward: q, k, v are E4M3 [B, H, N, d]; scales are powers of two per
-// block of rows (block_m for Q, block_n for K and V); o is bf16.
+// FP8 forward: q, k, v are E4M3 [B, H, N, d]; fp32 scales per block of
+// rows (32 for Q, 64 for K and V); o is bf16.
 struct Fp8FwdArgs {
   const void* q;
   const void* k;
@@ -62,15 +62,15 @@ struct Fp8FwdArgs {
   const float* v_scale;
   void* o;
   float* lse;  // may be null
-  int B, H, N, d, block_m, block_n;
+  int B, H, N, d;
   float scale;
   int causal;
 };
 
 hipError_t launch_fwd_fp8(const Fp8FwdArgs& a, hipStream_t s);
 
-// Block quantisation of a bf16 [B, H, N, d] tensor to E4M3 plus one
-// power-of-two scale per block of rows; signs (d values of +-1) turn on the
+// Block quantisation of a bf16 [B, H, N, d] tensor to E4M3 plus one fp32
+// scale (max|x| / 448) per block of rows; signs (d values of +-1) turn on the
 // Hadamard rotation.
 struct QuantArgs {
   const void* x;

@@ -217,17 +217,16 @@ attn_status attn_fwd_splitk_decode_paged(const void* q, const void* k_pool, cons
  * may be shorter).  Optionally every row is first rotated,
  * y = (x o signs) H / sqrt(d) with H the Sylvester Hadamard matrix (an
  * orthogonal map: rotating Q and K with the same signs leaves Q K^T
- * unchanged).  Each block gets one scale, the smallest power of two 2^k with
- * 448 * 2^k >= max|y| (k >= -126; 1 for an all-zero block), and its values
- * become e4m3(y / 2^k), rounded to nearest even.  The page's scale is
- * max|y| / 448; a power of two keeps y / scale exact and lets the matrix
- * unit apply the scale in attn_fwd_fp8.
+ * unchanged).  Each block gets the page's scale max|y| / 448 (an fp32
+ * division, correctly rounded; 1 for an all-zero block), and its values
+ * become e4m3(clamp(y / scale, -448, 448)), y / scale again an fp32 division,
+ * rounded to nearest even.
  *
  *   x          : [B, H, N, d] bf16
  *   signs      : d floats, each +1 or -1, DEVICE memory; NULL = no rotation
  *   x8         : [B, H, N, d] bytes (E4M3 bit patterns, written)
  *   scales     : [B, H, ceil(N / block_rows)] fp32 (written)
- *   block_rows : >= 1
+ *   block_rows : >= 1 (attn_fwd_fp8 takes 32 for Q and 64 for K and V)
  *
  * Supported: d in {64, 128}; the rotation for d == 64 only.
  * Errors: ATTN_ERR_INVALID_ARG for NULL or misaligned pointers (x, x8 16
@@ -239,31 +238,32 @@ attn_status attn_quantize_fp8(const void* x, const float* signs, void* x8, float
 
 /*
  * attn_fwd_fp8 -- attention forward on FP8 (E4M3) inputs with per-block
- * scales ("8. FlashAttention 实战", section 8.9.3): the two products run on
- * FP8 with fp32 accumulation, the softmax statistics in fp32, and the
- * probabilities are requantised to FP8 before the second product.
+ * scales, the method of "8. FlashAttention 实战", section 8.9.3 and the
+ * listing of section 8.9.6: both products run on FP8 with fp32
+ * accumulation, the softmax statistics in fp32, and the probabilities are
+ * requantised to FP8 with one scale per block before the second product.
  *
- * With the dequantised inputs q = q8 * sq, k = k8 * sk, v = v8 * sv (each
- * row's value times its block's scale), per query row i:
- *     u_j = scale * q_i . k_j * log2(e)             (masked if causal)
- *     a_j = 2^(u_j - M_i + 3)   with M_i an integer reference (the kernel
- *           takes the ceiling of a running row max)
- *     l_i = sum_j a_j                                (not rounded)
- *     O_i = sum_j e4m3(a_j) v_j / l_i,   LSE_i = (M_i + log2 l_i - 3) ln 2
- * E4M3 rounding commutes with scaling by powers of two, so the result does
- * not depend on the choice of M_i except for a_j below 2^-6 (the subnormal
- * range).  This replaces the page's data-dependent per-block scale of P with
- * a fixed one.
+ * Query rows are taken in blocks of BLOCK_M = 32 and keys in blocks of
+ * BLOCK_N = 64.  With q = q8 sq, k = k8 sk, v = v8 sv (each row's E4M3 value
+ * times its block's scale), for every (query block, key block) with a
+ * visible pair and every row of it, with the running state (m, l, U):
+ *     s       = scale * q . k                       (masked if causal)
+ *     m_new   = max(m, max s),  alpha = e^(m - m_new),  p = e^(s - m_new)
+ *     l       = alpha l + sum p
+ *     scale_p = (largest p of the block, over its rows below N) / 448
+ *     U       = alpha U + (e4m3(p / scale_p) v8) scale_p sv
+ * and O = U / l, LSE = m + ln l.  (The page's listing multiplies the whole
+ * accumulator by scale_p scale_v after the product; it is read as scaling the
+ * block's own product.)
  *
  *   q8, k8, v8 : [B, H, N, d] E4M3 bytes (as written by attn_quantize_fp8)
- *   q_scale    : [B, H, ceil(N / block_m)] fp32;  k_scale, v_scale:
- *                [B, H, ceil(N / block_n)] fp32.  Every scale must be a power
- *                of two in [2^-126, 2^127]: only its exponent field is read.
+ *   q_scale    : [B, H, ceil(N / 32)] fp32;  k_scale, v_scale:
+ *                [B, H, ceil(N / 64)] fp32; every scale positive and finite
  *   o          : [B, H, N, d] bf16 (written);  lse: [B, H, N] fp32 or NULL
- *   block_m    : a multiple of 32;  block_n: a multiple of 64
+ *   block_m, block_n : the scale block sizes; 32 and 64 are supported
  *
- * Supported: d == 64.
- * Errors as attn_fwd.
+ * Supported: d == 64, block_m == 32, block_n == 64.
+ * Errors as attn_fwd; ATTN_ERR_UNSUPPORTED for other d or block sizes.
  */
 attn_status attn_fwd_fp8(const void* q8, const void* k8, const void* v8, const float* q_scale,
                          const float* k_scale, const float* v_scale, void* o, float* lse, int B, int H,

@@ -245,8 +245,10 @@ def test_fwd_fp8_validation():
     assert call(ks=NULL) == INVALID
     assert call(vs=ctypes.c_void_p(0x10002)) == INVALID
     assert call(lse=ctypes.c_void_p(0x10002)) == INVALID
-    for bm, bn in ((0, 64), (16, 64), (48, 64), (32, 32), (32, 96), (32, 0)):
+    for bm, bn in ((0, 64), (32, 0), (-32, 64)):
         assert call(bm=bm, bn=bn) == INVALID, (bm, bn)
+    for bm, bn in ((16, 64), (64, 64), (128, 128), (32, 32), (32, 128)):
+        assert call(bm=bm, bn=bn) == UNSUPPORTED, (bm, bn)
     assert call(N=0) == INVALID
     assert call(sc=0.0) == INVALID
     assert call(d=128) == UNSUPPORTED
