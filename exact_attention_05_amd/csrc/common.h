@@ -259,4 +259,35 @@ __device__ __forceinline__ int xcd_remap(int hw_id, int total) {
   return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
 }
 
+constexpr int kCusPerXcd = 32;
+
+// Work order of the two-workgroups-per-CU kernels.  Each XCD takes a
+// contiguous range of R work ids (whole heads when R is a multiple of the
+// query tiles per head).  Causal query tiles differ in length, and when the
+// grid fits the chip at once (R = two per CU of the XCD), the workgroups in
+// positions k and k + R/2 of an XCD share a CU: the first half runs the
+// longest tiles of the XCD's heads in decreasing length and the second half
+// the rest in increasing length, so every CU gets one long and one short
+// tile.  Otherwise the longest tiles go first and the dispatcher balances.
+template <bool CAUSAL>
+__device__ __forceinline__ void causal_order(int hw_id, int total, int n_qtiles, int& bh, int& qtile) {
+  const int lid = xcd_remap(hw_id, total);
+  bh = lid / n_qtiles;
+  qtile = lid % n_qtiles;
+  if (!CAUSAL) return;
+  const int xcd = hw_id % kNumXcd, k = hw_id / kNumXcd;
+  const int q = total / kNumXcd, r = total % kNumXcd;
+  const int R = xcd < r ? q + 1 : q;
+  const int start = lid - k;
+  if (R == 2 * kCusPerXcd && R % n_qtiles == 0) {
+    const int nh = R / n_qtiles;
+    const int i = k < R / 2 ? k : R - 1 - (k - R / 2);  // rank in longest-first order
+    qtile = n_qtiles - 1 - i / nh;
+    bh = start / n_qtiles + i % nh;
+  } else {
+    qtile = n_qtiles - 1 - qtile;  // longest rows first
+  }
+}
+
+
 }  // namespace attn

@@ -111,10 +111,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   __shared__ __attribute__((aligned(1024))) unsigned char sb3[TB];
   __shared__ __attribute__((aligned(1024))) unsigned char sb4[TB];
 
-  const int lid = xcd_remap(blockIdx.x, total_wg);
-  const int bh = lid / n_qtiles;
-  int qtile = lid % n_qtiles;
-  if (CAUSAL) qtile = n_qtiles - 1 - qtile;  // longest rows first
+  int bh, qtile;
+  causal_order<CAUSAL>(blockIdx.x, total_wg, n_qtiles, bh, qtile);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;

@@ -57,7 +57,7 @@ def _empty_like_all(ins):
 def _outputs():
     f32 = torch.float32
     z = lambda *s, dtype=BF: torch.zeros(s, dtype=dtype, device=DEV)
-    nblk_q, nblk_k = -(-N // 64), -(-N // 64)
+    nblk_q, nblk_k = -(-N // 32), -(-N // 64)
     return {
         "o": z(B, H, N, D), "lse": z(B, H, N, dtype=f32),
         "oc": z(B, H, N, D), "lsec": z(B, H, N, dtype=f32),
@@ -87,10 +87,10 @@ def _pass(i, o):
     attn_fwd_splitk_decode(i["dq_"], i["dk_"], i["dv_"], S, out=o["do_"], lse=o["dlse"], workspace=o["dws"])
     attn_fwd_splitk_decode_paged(i["dq_"], i["kp"], i["vp"], i["tab"], i["lens"], S, out=o["po"], lse=o["plse"],
                                  workspace=o["pws"])
-    attn_quantize_fp8(i["q"], 64, out=o["q8"], scales=o["sq"])
+    attn_quantize_fp8(i["q"], 32, out=o["q8"], scales=o["sq"])
     attn_quantize_fp8(i["k"], 64, out=o["k8"], scales=o["sk"])
     attn_quantize_fp8(i["v"], 64, out=o["v8"], scales=o["sv"])
-    attn_fwd_fp8(o["q8"], o["k8"], o["v8"], o["sq"], o["sk"], o["sv"], 64, 64, causal=True, out=o["o8"],
+    attn_fwd_fp8(o["q8"], o["k8"], o["v8"], o["sq"], o["sk"], o["sv"], 32, 64, causal=True, out=o["o8"],
                  lse=o["lse8"])
     attn_bwd(i["q"], i["k"], i["v"], o["oc"], i["do"], o["lsec"], causal=True, dq=o["gq"], dk=o["gk"], dv=o["gv"],
              workspace=o["bws"])
