@@ -722,10 +722,14 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   }
 }
 
+// dQ for d = 64, run first: each workgroup also forms the per-row terms of
+// its 256 query rows (those of bwd_preprocess_kernel: D from the saved O and
+// dO, -LSE log2(e), and the two splits) and writes them for the dK/dV pass.
 template <bool CAUSAL>
 __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_dq_pp_kernel(
     const __bf16* __restrict__ Q, const __bf16* __restrict__ K, const __bf16* __restrict__ V,
-    const __bf16* __restrict__ dO, const float* __restrict__ nl2, const u32x2* __restrict__ dsplit,
+    const __bf16* __restrict__ dO, const __bf16* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ delta, float* __restrict__ nl2, u32x2* __restrict__ dsplit, u32x2* __restrict__ lsplit,
     __bf16* __restrict__ dQ, int N, int BH, int n_qtiles, int group, float scale, float scale_log2) {
   constexpr int D = 64;
   using T = TileLayout<D>;
@@ -772,8 +776,32 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     qB[ks] = qr < N ? *reinterpret_cast<const bf16x8*>(Q + base + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
     doB[ks] = qr < N ? *reinterpret_cast<const bf16x8*>(dO + base + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
   }
-  const float nlse2 = qr < N ? nl2[(int64_t)bh * N + qr] : kNegInf;
-  const u32x2 dwq = qr < N ? dsplit[(int64_t)bh * N + qr] : u32x2{0u, 0u};
+  // the row's terms: D = rowsum(dO o O) over the lane's 32 dims and its
+  // partner's (lane ^ 32), -LSE log2(e), and the splits of -D and of
+  // -LSE log2(e) / (scale log2(e))
+  float dpart = 0.f;
+  if (qr < N) {
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const u32x4 o = *reinterpret_cast<const u32x4*>(O + base + (int64_t)qr * D + 16 * ks + 8 * g);
+      const u32x4 d = bitcast<u32x4>(doB[ks]);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        dpart = fmaf(bf16lo_to_f32(o[w]), bf16lo_to_f32(d[w]), dpart);
+        dpart = fmaf(bf16hi_to_f32(o[w]), bf16hi_to_f32(d[w]), dpart);
+      }
+    }
+  }
+  const float drow = dpart + shfl_xor_f32(dpart, 32);
+  const int64_t row = (int64_t)bh * N + qr;
+  const float nlse2 = qr < N ? -LSE[row] * kLog2e : kNegInf;
+  const u32x2 dwq = qr < N ? split3_bf16(-drow) : u32x2{0u, 0u};
+  if (qr < N && g == 0) {
+    delta[row] = drow;
+    nl2[row] = nlse2;
+    dsplit[row] = dwq;
+    lsplit[row] = split3_bf16(nlse2 / scale_log2);
+  }
   const bf16x8 ndB = bitcast<bf16x8>(g == 0 ? u32x4{dwq[0], dwq[1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
   const bf16x8 ones3 = bitcast<bf16x8>(u32x4{0x3F803F80u, 0x3F80u, 0u, 0u});
   f32x16 dq[D / 32];
@@ -940,30 +968,35 @@ template <int D, bool CAUSAL>
 hipError_t run_bwd(const BwdArgs& a, hipStream_t s) {
   const int BH = a.B * a.H;
   const float scale_log2 = a.scale * kLog2e;
-  RowTerms rt;
-  hipError_t e = run_preprocess<D>(a, s, rt);
-  if (e != hipSuccess) return e;
-  float* nl2 = rt.nl2;
-  u32x2* dsplit = rt.dsplit;
-  u32x2* lsplit = rt.lsplit;
-
   const int group = BH >= kNumXcd ? BH / kNumXcd : 1;
+  hipError_t e;
   if constexpr (D == 64) {
+    // dQ first: it also writes the per-row terms that dK/dV reads
+    const int64_t rows = (int64_t)BH * a.N;
+    float* nl2 = a.delta + rows;
+    u32x2* dsplit = reinterpret_cast<u32x2*>(a.delta + 2 * rows);
+    u32x2* lsplit = dsplit + rows;
+    const int n_qt = (a.N + kPPWaves * 32 - 1) / (kPPWaves * 32);
+    hipLaunchKernelGGL((bwd_dq_pp_kernel<CAUSAL>), dim3(n_qt * BH), dim3(kPPThreads), 0, s,
+                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
+                       static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO),
+                       static_cast<const __bf16*>(a.o), a.lse, a.delta, nl2, dsplit, lsplit,
+                       static_cast<__bf16*>(a.dq), a.N, BH, n_qt, group, a.scale, scale_log2);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
     const int n_kt = (a.N + kPPWaves * 32 - 1) / (kPPWaves * 32);
     hipLaunchKernelGGL((bwd_dkdv_pp_kernel<CAUSAL>), dim3(n_kt * BH), dim3(kPPThreads), 0, s,
                        static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
                        static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), lsplit, dsplit,
                        static_cast<__bf16*>(a.dk), static_cast<__bf16*>(a.dv), a.N, BH, n_kt, group, a.scale,
                        scale_log2);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int n_qt = (a.N + kPPWaves * 32 - 1) / (kPPWaves * 32);
-    hipLaunchKernelGGL((bwd_dq_pp_kernel<CAUSAL>), dim3(n_qt * BH), dim3(kPPThreads), 0, s,
-                       static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
-                       static_cast<const __bf16*>(a.v), static_cast<const __bf16*>(a.dO), nl2, dsplit,
-                       static_cast<__bf16*>(a.dq), a.N, BH, n_qt, group, a.scale, scale_log2);
     return hipGetLastError();
   }
+  RowTerms rt;
+  e = run_preprocess<D>(a, s, rt);
+  if (e != hipSuccess) return e;
+  float* nl2 = rt.nl2;
+  u32x2* dsplit = rt.dsplit;
   const int n_kt = (a.N + kWaves * 32 - 1) / (kWaves * 32);
   hipLaunchKernelGGL((bwd_dkdv_kernel<D, CAUSAL>), dim3(n_kt * BH), dim3(kThreads), 0, s,
                      static_cast<const __bf16*>(a.q), static_cast<const __bf16*>(a.k),
