@@ -802,8 +802,11 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     dsplit[row] = dwq;
     lsplit[row] = split3_bf16(nlse2 / scale_log2);
   }
-  const bf16x8 ndB = bitcast<bf16x8>(g == 0 ? u32x4{dwq[0], dwq[1], 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
-  const bf16x8 ones3 = bitcast<bf16x8>(u32x4{0x3F803F80u, 0x3F80u, 0u, 0u});
+  // dP^T - D starts from -D: the lane's query is the accumulator's column,
+  // so all 16 of its elements start at the same value
+  f32x16 negd;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) negd[i] = -drow;
   f32x16 dq[D / 32];
 #pragma unroll
   for (int mt = 0; mt < D / 32; ++mt) dq[mt] = f32x16{};
@@ -833,10 +836,10 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
         for (int mt = 0; mt < D / 32; ++mt) tk[tt][mt] = of.tr(bprev, 2 * KP + tt, mt);
     }
     if (do_scores) {
-      dpacc = mfma32x32x16(ones3, ndB, f32x16{});
-      sacc = f32x16{};
+      sacc = mfma32x32x16(rk[0], qB[0], f32x16{});
+      dpacc = mfma32x32x16(rv[0], doB[0], negd);
 #pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
+      for (int ks = 1; ks < D / 16; ++ks) {
         sacc = mfma32x32x16(rk[ks], qB[ks], sacc);
         dpacc = mfma32x32x16(rv[ks], doB[ks], dpacc);
       }
@@ -849,7 +852,7 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     }
     if (do_acc && do_scores) {
       __builtin_amdgcn_sched_group_barrier(0x0100, 4 * (D / 32), 0);
-      __builtin_amdgcn_sched_group_barrier(0x0008, 1 + 2 * (D / 16) + 2 * (D / 32), 0);
+      __builtin_amdgcn_sched_group_barrier(0x0008, 2 * (D / 16) + 2 * (D / 32), 0);
     }
     __builtin_amdgcn_s_setprio(0);
   };
