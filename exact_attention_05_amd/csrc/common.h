@@ -242,6 +242,47 @@ struct TileCopy {
   }
 };
 
+// 16 bytes per lane from byte voff of the `bytes`-long buffer at src to LDS
+// at lds_base + 16 * lane (buffer_load_dwordx4 ... lds).  The hardware checks
+// voff against the buffer's length and reads zeros past its end; src and
+// bytes are wave-uniform, so the descriptor is built with scalar
+// instructions.
+__device__ __forceinline__ void buffer_to_lds16(const void* src, uint32_t bytes, int voff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(src), (short)0, (int)bytes, 0x00020000),
+      (lds_void*)lds_base, 16, voff, 0, 0, 0);
+}
+
+// TileCopy through buffer descriptors: each tile gets a descriptor that
+// starts at its first row and ends at row nrows, so the lane's fixed offset
+// inside the tile needs no per-tile vector arithmetic and rows past nrows
+// read zeros.
+template <int D, int NW>
+struct TileCopyBuf {
+  using T = TileLayout<D>;
+  static constexpr int kPerWave = (D / 8 + NW - 1) / NW;
+  int voff[kPerWave], dst[kPerWave];
+  bool on[kPerWave];
+  __device__ __forceinline__ TileCopyBuf(int wave, int lane) {
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i) {
+      const int c = wave + NW * i;
+      on[i] = c < D / 8;
+      const int line = 4 * c + (lane >> 4);
+      int k, ch;
+      T::at(on[i] ? line : 0, lane & 15, k, ch);
+      voff[i] = (k * D + 8 * ch) * 2;
+      dst[i] = 4 * c * 256;
+    }
+  }
+  __device__ __forceinline__ void issue(const __bf16* src, int nrows, int r0, unsigned char* tile) const {
+    const uint32_t bytes = (uint32_t)(nrows - r0) * (uint32_t)(D * 2);  // r0 < nrows
+#pragma unroll
+    for (int i = 0; i < kPerWave; ++i)
+      if (on[i]) buffer_to_lds16(src + (int64_t)r0 * D, bytes, voff[i], tile + dst[i]);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Launch-order remap for 8 XCDs.
 // Consecutive workgroup ids are handed to the XCDs round-robin, and each XCD

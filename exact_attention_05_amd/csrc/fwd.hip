@@ -602,11 +602,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int ntiles = (kend + kBc - 1) / kBc;
 
   // each wavefront copies one 1 KB piece of the K tile and one of the V tile
-  // (two direct-to-LDS copies per tile)
-  const TileCopy<D, NW> cp(wave, lane);
+  // (two direct-to-LDS buffer loads per tile; keys past N read zeros)
+  const TileCopyBuf<D, NW> cp(wave, lane);
   auto issue_tile = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
-    cp.issue(K + base, j * kBc, N, buf);
-    cp.issue(V + base, j * kBc, N, buf + T::kBytes);
+    cp.issue(K + base, N, j * kBc, buf);
+    cp.issue(V + base, N, j * kBc, buf + T::kBytes);
   };
 
   issue_tile(0, sb0);
