@@ -545,21 +545,21 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const int kw0 = k0 + wave * 32;
   const int key = kw0 + l32;
 
-  const TileCopy<D, NW> cp(wave, lane);
+  const TileCopyBuf<D, NW> cp(wave, lane);
   const TileOffsets<D> of(lane);
   // wavefronts 0-1 copy the tile's dsplit, 2-3 its lsplit (2 words per row, 32 rows each)
   const uint32_t* sph = reinterpret_cast<const uint32_t*>((wave < 2 ? dsplit : lsplit) + (int64_t)bh * N);
   auto issue_tile = [&](int it, unsigned char* buf) __attribute__((always_inline)) {
     const int q0 = it * kT;
-    cp.issue(Q + base, q0, N, buf);
-    cp.issue(dO + base, q0, N, buf + T::kBytes);
+    cp.issue(Q + base, N, q0, buf);
+    cp.issue(dO + base, N, q0, buf + T::kBytes);
     if (wave < 4) {
       const int w = 64 * (wave & 1) + lane;
       const int r = min(q0 + (w >> 1), N - 1);
       global_to_lds4(sph + 2 * r + (w & 1), buf + 2 * T::kBytes + 256 * wave);
     }
   };
-  constexpr int kCopies = 2 * TileCopy<D, NW>::kPerWave;
+  constexpr int kCopies = 2 * TileCopyBuf<D, NW>::kPerWave;
   // wait for this wavefront's copies of all tiles but the newest one
   // (one_after) or of all tiles
   auto wait_copies = [&](bool one_after) __attribute__((always_inline)) {
@@ -754,13 +754,13 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const int qw0 = q0 + wave * 32;
   const int qr = qw0 + l32;
 
-  const TileCopy<D, NW> cp(wave, lane);
+  const TileCopyBuf<D, NW> cp(wave, lane);
   const TileOffsets<D> of(lane);
   auto issue_tile = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
-    cp.issue(K + base, j * kT, N, buf);
-    cp.issue(V + base, j * kT, N, buf + T::kBytes);
+    cp.issue(K + base, N, j * kT, buf);
+    cp.issue(V + base, N, j * kT, buf + T::kBytes);
   };
-  constexpr int kCopies = 2 * TileCopy<D, NW>::kPerWave;
+  constexpr int kCopies = 2 * TileCopyBuf<D, NW>::kPerWave;
   auto wait_copies = [&](bool one_after) __attribute__((always_inline)) {
     if (one_after) wait_vm_at_most<kCopies>(); else wait_vm_at_most<0>();
   };

@@ -170,14 +170,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   auto issue_tile_copy = [&](int kb, int buf) {
     unsigned char* kt = ring(buf);
     unsigned char* vt = kt + T::kBytes;
+    // one buffer descriptor per tile: keys past N read zeros (masked out)
+    const uint32_t bytes = (uint32_t)(N - kb) * (uint32_t)(D * 2);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      // rows past the end read row N-1 (valid memory); they are masked out
-      const int row = min(kb + ld_key[i], N - 1);
-      const int64_t off = (int64_t)row * D + ld_col[i];
+      const int voff = (ld_key[i] * D + ld_col[i]) * 2;
       const int lds_line = 4 * (wave * NLD + i);
-      global_to_lds16(Kh + off, kt + lds_line * 256);
-      global_to_lds16(Vh + off, vt + lds_line * 256);
+      buffer_to_lds16(Kh + (int64_t)kb * D, bytes, voff, kt + lds_line * 256);
+      buffer_to_lds16(Vh + (int64_t)kb * D, bytes, voff, vt + lds_line * 256);
     }
   };
 

@@ -133,12 +133,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   // lane l fills physical chunk l % 4 of row 16 (wave % 4) + l / 4.
   const uint8_t* csrc = (wave < 4 ? K : V) + base;  // wave-uniform
   const int crow = 16 * (wave & 3) + (lane >> 2);
-  const int ccol = 16 * ((lane & 3) ^ ((crow >> 2) & 3));
+  const int cvoff = crow * kFp8Row + 16 * ((lane & 3) ^ ((crow >> 2) & 3));
   const int cdst = (wave < 4 ? 0 : kFp8Tile) + 1024 * (wave & 3);
   auto issue_tile = [&](int j, unsigned char* buf) __attribute__((always_inline)) {
-    // rows past N read row N-1 (masked later); a head spans < 2^31 bytes
-    const uint32_t off = (uint32_t)(min(j * kFp8Bc + crow, N - 1) * kFp8Row + ccol);
-    global_to_lds16(csrc + off, buf + cdst);
+    // one buffer descriptor per tile: rows past N read zeros (masked later)
+    const int r0 = j * kFp8Bc;
+    buffer_to_lds16(csrc + (int64_t)r0 * kFp8Row, (uint32_t)(N - r0) * kFp8Row, cvoff, buf + cdst);
   };
 
   issue_tile(0, sb0);
