@@ -8,7 +8,9 @@ Turns the CSV files that ``rocprofv3 --kernel-trace --stats`` and
 * HBM traffic per launch from ``FETCH_SIZE`` / ``WRITE_SIZE`` (KiB per
   dispatch), each scaled by what the same counter reads for a plain device
   copy of known size in the same run;
-* instruction mix (VALU, transcendental, MFMA, LDS) from the SQ counters.
+* instruction mix (VALU, transcendental, MFMA, LDS) from the SQ counters;
+* the shader clock under load from ``SQ_BUSY_CU_CYCLES`` and the dispatch
+  durations.
 
 Only parsing happens here; the profiler itself runs as its own command with
 the program after ``--``.  Usage::
@@ -17,6 +19,7 @@ the program after ``--``.  Usage::
     python -m exact_attention_05_amd.rocprof_report traffic --fetch DIR --write DIR \
         --kernel REGEX --calib-mib 256 --key NAME --sources fwd.hip,common.h --cmd C
     python -m exact_attention_05_amd.rocprof_report counters DIR --kernel REGEX
+    python -m exact_attention_05_amd.rocprof_report clock DIR --kernel REGEX --key NAME --sources fwd.hip,common.h --cmd C
 """
 
 import argparse
@@ -231,6 +234,47 @@ def cmd_counters(a):
         print(f"\nVALU instructions per MFMA instruction: {got['SQ_INSTS_VALU'] / got['SQ_INSTS_MFMA']:.2f}")
 
 
+def cmd_clock(a):
+    """Average shader clock of a kernel under load: SQ_BUSY_CU_CYCLES per
+    dispatch over the 256 CUs, divided by the dispatch's duration (both from
+    the same --pmc run's counter CSV)."""
+    rows = []
+    with open(_find(a.dir, "counter_collection.csv")) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == "SQ_BUSY_CU_CYCLES" and re.search(a.kernel, r["Kernel_Name"]):
+                ns = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                rows.append((float(r["Counter_Value"]) / a.cus, ns))
+    if not rows:
+        raise KeyError(f"no SQ_BUSY_CU_CYCLES values for kernels matching {a.kernel!r}")
+    cyc = sum(c for c, _ in rows) / len(rows)
+    ns = sum(n for _, n in rows) / len(rows)
+    ghz = cyc / ns
+    path = os.path.join(ROOT, "profiles", "clock.json")
+    tab = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            tab = json.load(f)
+    srcs = a.sources.split(",")
+    tab[a.key] = {"clock_ghz": round(ghz, 4), "busy_cycles_per_cu": round(cyc), "avg_ns": round(ns),
+                  "dispatches": len(rows), "kernel_regex": a.kernel, "sources": srcs, "source_sha": src_sha(srcs)}
+    with open(path, "w") as f:
+        json.dump(tab, f, indent=1, sort_keys=True)
+        f.write("\n")
+    lines = [
+        f"# Shader clock under load of `{a.kernel}` ({a.key})", "", "Command (MI355X host, repository root):", "",
+        "```", a.cmd, "```", "",
+        "| dispatches | SQ_BUSY_CU_CYCLES / CU | duration (ns) | clock (GHz) |", "|---|---|---|---|",
+        f"| {len(rows)} | {cyc:.0f} | {ns:.0f} | {ghz:.3f} |", "",
+        f"At this clock the dense bf16 MFMA peak is 256 CU x 4 SIMD x 1024 FLOP/clk x {ghz:.3f} GHz = "
+        f"{256 * 4 * 1024 * ghz / 1e3:.1f} TFLOP/s ({100 * ghz / 2.4:.1f}% of the 2.4 GHz figure).",
+    ]
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -252,6 +296,15 @@ def main(argv=None):
     t.add_argument("--algorithmic", type=float, default=0.0)
     t.add_argument("--out")
     t.set_defaults(fn=cmd_traffic)
+    k = sub.add_parser("clock")
+    k.add_argument("dir")
+    k.add_argument("--kernel", required=True)
+    k.add_argument("--key", required=True)
+    k.add_argument("--sources", required=True)
+    k.add_argument("--cmd", required=True)
+    k.add_argument("--cus", type=int, default=256)
+    k.add_argument("--out")
+    k.set_defaults(fn=cmd_clock)
     c = sub.add_parser("counters")
     c.add_argument("dir")
     c.add_argument("--kernel", required=True)
