@@ -20,6 +20,8 @@ the program after ``--``.  Usage::
         --kernel REGEX --calib-mib 256 --key NAME --sources fwd.hip,common.h --cmd C
     python -m exact_attention_05_amd.rocprof_report counters DIR --kernel REGEX
     python -m exact_attention_05_amd.rocprof_report clock DIR --kernel REGEX --key NAME --sources fwd.hip,common.h --cmd C
+    python -m exact_attention_05_amd.rocprof_report cycles --run LABEL=DIR:TILES ... --kernel REGEX --title T --cmd C ...
+    python -m exact_attention_05_amd.rocprof_report utilisation --a DIR --b DIR --kernel LABEL=REGEX ... --title T --cmd C ...
 """
 
 import argparse
@@ -275,6 +277,92 @@ def cmd_clock(a):
     print(text)
 
 
+def cmd_cycles(a):
+    """Instructions and cycles of one kernel across runs (different sizes or
+    inputs): per-wavefront instruction counts, busy cycles per CU, duration and
+    clock of each run, and the per-tile increments between the first two runs
+    (the loop's cost, free of the per-wavefront prologue and epilogue)."""
+    want = ["SQ_WAVES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_SALU",
+            "SQ_BUSY_CU_CYCLES"]
+    runs = []
+    for spec in a.run:
+        label, rest = spec.rsplit("=", 1)
+        d, tiles = rest.rsplit(":", 1)
+        per = collections.defaultdict(dict)  # dispatch -> counter -> value, plus its duration
+        with open(_find(d, "counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                if re.search(a.kernel, r["Kernel_Name"]):
+                    e = per[r["Dispatch_Id"]]
+                    e[r["Counter_Name"]] = float(r["Counter_Value"])
+                    e["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if not per:
+            raise KeyError(f"no dispatches of kernels matching {a.kernel!r} in {d}")
+        mean = {c: sum(e[c] for e in per.values()) / len(per) for c in want + ["ns"]}
+        runs.append((label, int(tiles), len(per), mean))
+    lines = [f"# Instructions and cycles of `{a.kernel}` ({a.title})", "", "Commands (MI355X host, repository root):",
+             "", "```", *a.cmd, "```", "",
+             "| run | dispatches | waves | tiles per wave | VALU / wave | MFMA / wave | transcendental / wave | "
+             "SALU / wave | busy cycles / CU | duration (us) | clock (GHz) |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for label, tiles, n, m in runs:
+        w = m["SQ_WAVES"]
+        cyc = m["SQ_BUSY_CU_CYCLES"] / a.cus
+        lines.append(f"| {label} | {n} | {w:.0f} | {tiles} | {m['SQ_INSTS_VALU'] / w:.1f} | {m['SQ_INSTS_MFMA'] / w:.1f} | "
+                     f"{m['SQ_INSTS_VALU_TRANS_F32'] / w:.1f} | {m['SQ_INSTS_SALU'] / w:.1f} | {cyc:.0f} | "
+                     f"{m['ns'] / 1e3:.1f} | {cyc / m['ns']:.3f} |")
+    if len(runs) >= 2:
+        (la, ta, _, ma), (lb, tb, _, mb) = runs[0], runs[1]
+        dt = tb - ta
+        inc = {c: (mb[c] / mb["SQ_WAVES"] - ma[c] / ma["SQ_WAVES"]) / dt for c in want[1:5]}
+        fixed = ma["SQ_INSTS_VALU"] / ma["SQ_WAVES"] - inc["SQ_INSTS_VALU"] * ta
+        lines += ["", f"Per tile and wavefront (from {la} and {lb}): {inc['SQ_INSTS_VALU']:.1f} VALU instructions, of "
+                  f"which {inc['SQ_INSTS_MFMA']:.1f} MFMA (SQ_INSTS_VALU counts them) and "
+                  f"{inc['SQ_INSTS_VALU_TRANS_F32']:.1f} transcendental, so "
+                  f"{inc['SQ_INSTS_VALU'] - inc['SQ_INSTS_MFMA']:.1f} other vector instructions; "
+                  f"{inc['SQ_INSTS_SALU']:.1f} scalar. Per wavefront outside the loop: {fixed:.0f} VALU instructions."]
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def cmd_utilisation(a):
+    """Per-SIMD split of a kernel's cycles from the two --pmc passes: matrix
+    unit busy (SQ_VALU_MFMA_BUSY_CYCLES), VALU issuing (SQ_ACTIVE_INST_VALU,
+    4-cycle units), both at once (SQ_VALU_MFMA_COEXEC_CYCLES) and neither,
+    against the launch's cycles (SQ_BUSY_CU_CYCLES per CU); the raw means
+    follow."""
+    simds = 4 * a.cus
+    lines = [f"# {a.title}", "", "Commands (MI355X host, repository root):", "", "```", *a.cmd, "```", "",
+             "Per SIMD: SQ_ACTIVE_INST_VALU x 4 / SIMDs (4-cycle units), SQ_VALU_MFMA_BUSY_CYCLES and "
+             "SQ_VALU_MFMA_COEXEC_CYCLES / SIMDs, SQ_BUSY_CU_CYCLES / CUs = the cycles of the launch "
+             f"({a.cus} CUs, {simds} SIMDs).", "",
+             "| kernel | cycles | MFMA busy | VALU issuing | both at once | neither |", "|---|---|---|---|---|---|"]
+    raw = []
+    for spec in a.kernel:
+        label, regex = spec.split("=", 1)
+        va, vb = counter_values(a.a), counter_values(a.b)
+        cyc = _match(va, regex, "SQ_BUSY_CU_CYCLES")[0] / a.cus
+        valu = _match(va, regex, "SQ_ACTIVE_INST_VALU")[0] * 4 / simds
+        mfma = _match(vb, regex, "SQ_VALU_MFMA_BUSY_CYCLES")[0] / simds
+        both = _match(vb, regex, "SQ_VALU_MFMA_COEXEC_CYCLES")[0] / simds
+        neither = cyc - (mfma + valu - both)
+        pct = lambda x: f"{100 * x / cyc:.0f}%"
+        lines.append(f"| {label} | {cyc / 1e3:.0f} k | {pct(mfma)} | {pct(valu)} | {pct(both)} | {pct(neither)} |")
+        raw.append((label, regex, va, vb))
+    for label, regex, va, vb in raw:
+        lines += ["", f"## {label}", "", "| counter | mean per dispatch |", "|---|---|"]
+        for vals in (va, vb):
+            for c in sorted({c for (k, c) in vals if re.search(regex, k)}):
+                lines.append(f"| {c} | {_match(vals, regex, c)[0]:.1f} |")
+    text = "\n".join(lines) + "\n"
+    if a.out:
+        with open(a.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -305,6 +393,23 @@ def main(argv=None):
     k.add_argument("--cus", type=int, default=256)
     k.add_argument("--out")
     k.set_defaults(fn=cmd_clock)
+    y = sub.add_parser("cycles")
+    y.add_argument("--run", action="append", required=True, help="LABEL=DIR:TILES_PER_WAVE (a --pmc run)")
+    y.add_argument("--kernel", required=True)
+    y.add_argument("--title", required=True)
+    y.add_argument("--cmd", action="append", required=True)
+    y.add_argument("--cus", type=int, default=256)
+    y.add_argument("--out")
+    y.set_defaults(fn=cmd_cycles)
+    w = sub.add_parser("utilisation")
+    w.add_argument("--a", required=True, help="pass with SQ_ACTIVE_INST_VALU and SQ_BUSY_CU_CYCLES")
+    w.add_argument("--b", required=True, help="pass with SQ_VALU_MFMA_BUSY_CYCLES and SQ_VALU_MFMA_COEXEC_CYCLES")
+    w.add_argument("--kernel", action="append", required=True, help="LABEL=REGEX")
+    w.add_argument("--title", required=True)
+    w.add_argument("--cmd", action="append", required=True)
+    w.add_argument("--cus", type=int, default=256)
+    w.add_argument("--out")
+    w.set_defaults(fn=cmd_utilisation)
     c = sub.add_parser("counters")
     c.add_argument("dir")
     c.add_argument("--kernel", required=True)

@@ -60,6 +60,26 @@ def test_decode_small(L, S, d):
     _check_partials(ws, B, H, d, S, qq, kk, vv, scale)
 
 
+@pytest.mark.parametrize("B,H,L,S", [(2, 32, 40000, 256), (4, 16, 100, 256), (4, 16, 3001, 128)])
+def test_decode_large_grids(B, H, L, S):
+    """Grids of 8192 chunks and more: long chunks (156 keys), mostly empty
+    chunks (L < S) and a ragged split, every head and partial against the
+    oracle."""
+    _say(f"decode large grid B={B} H={H} L={L} S={S}")
+    d = 128
+    q = make_tensor(L + S + 1, "q", B, H, 1, d, torch.bfloat16)
+    k = make_tensor(L + S + 1, "k", B, H, L, d, torch.bfloat16)
+    v = make_tensor(L + S + 1, "v", B, H, L, d, torch.bfloat16)
+    scale = 1.0 / math.sqrt(d)
+    o, lse, ws = attn_fwd_splitk_decode(q.to(DEV), k.to(DEV), v.to(DEV), S, scale=scale)
+    torch.cuda.synchronize()
+    qq, kk, vv = widen(q), widen(k), widen(v)
+    O, LSE = ref_fwd(qq, kk, vv, scale, False)
+    assert_bar("O", widen(o), O, torch.bfloat16)
+    assert_lse("LSE", widen(lse), LSE[..., 0])
+    _check_partials(ws, B, H, d, S, qq, kk, vv, scale)
+
+
 def test_decode_properties():
     """V = ones gives O = 1; q = 0 gives the mean of V and LSE = ln L."""
     _say("decode properties")

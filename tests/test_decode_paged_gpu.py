@@ -89,6 +89,26 @@ def test_paged_decode_ragged(bs, S, d):
     _check_partials(ws, Q, KP, VP, tab.numpy(), lens.numpy(), S, scale)
 
 
+def test_paged_decode_large_grid():
+    """8192 chunks over 128 heads, ragged lengths (an empty sequence, a single
+    token) and a scattered table."""
+    B, H, d, bs, S = 4, 32, 64, 16, 64
+    _say(f"paged decode large grid B={B} H={H} S={S}")
+    max_blocks = 40
+    q, kp, vp, tab = _inputs(77, B, H, d, bs, max_blocks)
+    full = max_blocks * bs
+    lens = torch.tensor([0, 1, 2 * bs + 5, full], dtype=torch.int32)
+    for b in range(B):
+        tab[b, (int(lens[b]) + bs - 1) // bs:] = -1
+    scale = 1.0 / math.sqrt(d)
+    o, lse, ws = _run(q, kp, vp, tab, lens, S, scale)
+    Q, KP, VP = widen(q), widen(kp), widen(vp)
+    O, LSE = ref_paged_decode(Q, KP, VP, tab.numpy(), lens.numpy(), scale)
+    assert_bar("O", widen(o), O, torch.bfloat16)
+    assert_lse("LSE", widen(lse), LSE[..., 0])
+    _check_partials(ws, Q, KP, VP, tab.numpy(), lens.numpy(), S, scale)
+
+
 @pytest.mark.parametrize("d", [64, 128])
 def test_paged_identity_table_equals_dense_bitwise(d):
     """With the dense cache cut into blocks in order (an identity table) and
