@@ -68,12 +68,28 @@ __device__ __forceinline__ int fp8_off(int k, int c) { return 64 * k + 16 * (c ^
 // accumulator's row order (block J / 16, accumulator index J % 16).
 __device__ __forceinline__ constexpr int pkey(int h, int J) { return 32 * (J >> 4) + acc_row(J & 15, h); }
 
+// v_max_f32 / v_max3_f32 as plain instructions.  The compiler puts a
+// canonicalising v_max_f32 x, x, x in front of every fmaxf operand it cannot
+// prove canonical (MFMA results, lane reads), which doubles the per-tile row
+// max.  The operands here are never signalling NaNs; on quiet NaNs and
+// infinities the instructions give what fmaxf gives.
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // v_permlane32_swap of x with itself: the first result holds x of lanes
 // 0-31 in both halves of the wave, the second x of lanes 32-63; a symmetric
 // combination of the two is the lane pair's (l, l ^ 32) value in every lane.
 __device__ __forceinline__ float max_of_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float sum_of_halves(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -82,10 +98,13 @@ __device__ __forceinline__ float sum_of_halves(float x) {
 
 // Max of `x` over lanes 0-31 (lanes 32-63 hold the same values), wave-uniform.
 __device__ __forceinline__ float max_over_32_lanes(float x) {
-  x = fmaxf(x, __builtin_amdgcn_update_dpp(kNegInf, x, 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
-  x = fmaxf(x, __builtin_amdgcn_update_dpp(kNegInf, x, 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
-  x = fmaxf(x, __builtin_amdgcn_update_dpp(kNegInf, x, 0x141, 0xF, 0xF, false));  // row_half_mirror
-  x = fmaxf(x, __builtin_amdgcn_update_dpp(kNegInf, x, 0x140, 0xF, 0xF, false));  // row_mirror
+  // every source lane of these patterns lies in the destination's row
+#define ATTN_DPP(v, ctrl) __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, true))
+  x = vmax(x, ATTN_DPP(x, 0xB1));   // quad_perm 1,0,3,2
+  x = vmax(x, ATTN_DPP(x, 0x4E));   // quad_perm 2,3,0,1
+  x = vmax(x, ATTN_DPP(x, 0x141));  // row_half_mirror
+  x = vmax(x, ATTN_DPP(x, 0x140));  // row_mirror
+#undef ATTN_DPP
   return fmaxf(__uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 0)),
                __uint_as_float(__builtin_amdgcn_readlane(__float_as_uint(x), 16)));
 }
@@ -252,12 +271,15 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   auto vph = [&](int j) __attribute__((always_inline)) {
     mask_tile(j);
     // row max of the raw scores (the block's scales are positive)
-    float mx = kNegInf;
+    float mx0 = kNegInf, mx1 = kNegInf;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) mx = fmaxf(mx, fmaxf(sacc[0][i], sacc[1][i]));
-    mx = max_of_halves(mx);
+    for (int i = 0; i < 16; i += 2) {
+      mx0 = vmax3(mx0, sacc[0][i], sacc[1][i]);
+      mx1 = vmax3(mx1, sacc[0][i + 1], sacc[1][i + 1]);
+    }
+    const float mx = max_of_halves(vmax(mx0, mx1));
     const float bm = mx * ck;  // the row's largest u in this block (-inf: none visible)
-    const float m_new = fmaxf(m, bm);
+    const float m_new = vmax(m, bm);
     const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m - m_new);
     // e = log2 of the block's largest p, over its rows below N
     const float e = max_over_32_lanes(qr < N ? bm - m_new : kNegInf);
