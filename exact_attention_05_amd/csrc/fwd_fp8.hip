@@ -192,7 +192,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   float m = kNegInf, lsum = 0.f;
   float alpha_prev = 1.f, f_prev = 0.f;  // the previous tile's alpha (per row) and scale_p sv (per wavefront)
   f32x16 sacc[2];
-  i32x8 pb;  // P8 of the current tile, the B operand of T
+  i32x8 pb = {};  // P8 of the current tile, the B operand of T
   float ck = cq * ksh[0];
 
   // MFMA operands, all read from LDS at the top of the matrix phase so that
@@ -292,7 +292,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       for (int q = 0; q < 4; ++q) x[q] = fast_exp2(fmaf(sacc[w >> 2][4 * (w & 3) + q], ck, -off));
       if ((w & 1) == 0) r4[w >> 1] = (x[0] + x[1]) + (x[2] + x[3]);
       else r4[w >> 1] += (x[0] + x[1]) + (x[2] + x[3]);
-      const int pw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+      // both halves of the word are written: the previous tile's codes (read
+      // by the last matrix phase) only stand in for the old value
+      const int pw = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], pb[w], false);
       pb[w] = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], pw, true);
     }
     const float rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
