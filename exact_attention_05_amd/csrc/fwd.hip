@@ -609,14 +609,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     cp.issue(V + base, N, j * kBc, buf + T::kBytes);
   };
 
-  issue_tile(0, sb0);
-  if (ntiles > 1) issue_tile(1, sb1);
-  if (ntiles > 2) issue_tile(2, sb2);
-
+  // Q first: loads complete in issue order, so the first step waits for Q
+  // and tile 0 only
   bf16x8 qB[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks)
     qB[ks] = qr < N ? *reinterpret_cast<const bf16x8*>(Q + base + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
+  issue_tile(0, sb0);
 
   const TileOffsets<D> of(lane);
   f32x16 oacc[D / 32];
@@ -707,12 +706,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     asm volatile("" : "+v"(pb[0]), "+v"(pb[1]), "+v"(pb[2]), "+v"(pb[3]));
   };
 
-  // Tile 0 must have landed before the first barrier (tiles 1 and 2 may not).
-  if (ntiles > 2) wait_vm_at_most<4>(); else if (ntiles > 1) wait_vm_at_most<2>(); else wait_vm_at_most<0>();
+  // Q and tile 0 land before the first barrier; tiles 1-3 are issued after
+  // the first products (a copy in flight there makes the compiler wait for
+  // every load before them)
+  wait_vm_at_most<0>();
   lds_barrier();
   if (!lead) lds_barrier();
-  if (ntiles > 3) issue_tile(3, sb3);
   mph(sb0, sb0, false, true);
+  if (ntiles > 1) issue_tile(1, sb1);
+  if (ntiles > 2) issue_tile(2, sb2);
+  if (ntiles > 3) issue_tile(3, sb3);
   // tile 1 (tiles 2 and 3 may still be in flight)
   if (ntiles > 3) wait_vm_at_most<4>(); else if (ntiles > 2) wait_vm_at_most<2>(); else wait_vm_at_most<0>();
   lds_barrier();

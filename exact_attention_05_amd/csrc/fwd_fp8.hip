@@ -160,10 +160,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     buffer_to_lds16(csrc + (int64_t)r0 * kFp8Row, (uint32_t)(N - r0) * kFp8Row, cvoff, buf + cdst);
   };
 
-  issue_tile(0, sb0);
-  if (ntiles > 1) issue_tile(1, sb1);
-  if (ntiles > 2) issue_tile(2, sb2);
-
   // Q row of this lane: bytes 32g .. 32g+31 (the B operand's reduction half g)
   i32x8 qB = {};
   if (qr < N) {
@@ -171,6 +167,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const u32x4 a = qp[0], b = qp[1];
     qB = i32x8{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
   }
+  issue_tile(0, sb0);
   // the wavefront's 32 rows are one Q scale block
   const float cq = scale_log2 * QS[(int64_t)bh * ((N + 31) / 32) + min(qw0, N - 1) / 32];
 
@@ -307,10 +304,16 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     asm volatile("" : "+v"(pb));
   };
 
-  if (ntiles > 2) wait_vm_at_most<2>(); else if (ntiles > 1) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
+  // Q and tile 0 land before the first barrier; tiles 1-3 are issued after
+  // the first products (a copy in flight there makes the compiler wait for
+  // every load before them)
+  wait_vm_at_most<0>();
   lds_barrier();
   if (!lead) lds_barrier();
-  mph(sb0, sb0, false, true, [&]() __attribute__((always_inline)) { if (ntiles > 3) issue_tile(3, sb3); });
+  mph(sb0, sb0, false, true, []() __attribute__((always_inline)) {});
+  if (ntiles > 1) issue_tile(1, sb1);
+  if (ntiles > 2) issue_tile(2, sb2);
+  if (ntiles > 3) issue_tile(3, sb3);
   if (ntiles > 3) wait_vm_at_most<2>(); else if (ntiles > 2) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
   lds_barrier();
   vph(0);
