@@ -572,15 +572,15 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 
   const int i_begin = CAUSAL ? k0 / kT : 0;
   const int ntiles = (N + kT - 1) / kT - i_begin;
-  issue_tile(i_begin, sb0);
-  if (ntiles > 1) issue_tile(i_begin + 1, sb1);
-
+  // this wavefront's K and V rows first, then the first tile (loads
+  // complete in issue order)
   bf16x8 kB[D / 16], vB[D / 16];
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     kB[ks] = key < N ? *reinterpret_cast<const bf16x8*>(K + base + (int64_t)key * D + 16 * ks + 8 * g) : bf16x8{};
     vB[ks] = key < N ? *reinterpret_cast<const bf16x8*>(V + base + (int64_t)key * D + 16 * ks + 8 * g) : bf16x8{};
   }
+  issue_tile(i_begin, sb0);
   const bf16x8 ones3 = bitcast<bf16x8>(g == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -673,12 +673,16 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   };
 
   // Tile 0.
-  wait_copies(ntiles > 1);
+  // the first tile before the first barrier; the next two go out after the
+  // first products (a copy in flight there makes the compiler wait for every
+  // load)
+  wait_vm_at_most<0>();
   lds_barrier();
   if (!lead) lds_barrier();
-  if (ntiles > 2) issue_tile(i_begin + 2, sb2);
   read_rows(0, sb0);
   mph(0, sb0, false, true);
+  if (ntiles > 1) issue_tile(i_begin + 1, sb1);
+  if (ntiles > 2) issue_tile(i_begin + 2, sb2);
   lds_barrier();
   vph(i_begin * kT, true, 1, sb0);
   if (ntiles > 1) wait_copies(ntiles > 2);
@@ -767,34 +771,37 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
 
   const int kend = CAUSAL ? min(N, q0 + BQ) : N;
   const int ntiles = (kend + kT - 1) / kT;
-  issue_tile(0, sb0);
-  if (ntiles > 1) issue_tile(1, sb1);
 
+  // The rows of this wavefront first (Q, dO, O, LSE), then tile 0: loads
+  // complete in issue order, so the row terms wait for the rows only.
   bf16x8 qB[D / 16], doB[D / 16];
+  u32x4 orow[D / 16];
+  const int64_t row = (int64_t)bh * N + qr;
 #pragma unroll
   for (int ks = 0; ks < D / 16; ++ks) {
     qB[ks] = qr < N ? *reinterpret_cast<const bf16x8*>(Q + base + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
     doB[ks] = qr < N ? *reinterpret_cast<const bf16x8*>(dO + base + (int64_t)qr * D + 16 * ks + 8 * g) : bf16x8{};
+    orow[ks] = qr < N ? *reinterpret_cast<const u32x4*>(O + base + (int64_t)qr * D + 16 * ks + 8 * g) : u32x4{};
   }
+  const float lse = LSE[(int64_t)bh * N + min(qr, N - 1)];  // unconditional: no branch to wait in
+  issue_tile(0, sb0);
+  __builtin_amdgcn_sched_barrier(0);  // tile 0 goes out before the wait for the rows
   // the row's terms: D = rowsum(dO o O) over the lane's 32 dims and its
   // partner's (lane ^ 32), -LSE log2(e), and the splits of -D and of
   // -LSE log2(e) / (scale log2(e))
   float dpart = 0.f;
-  if (qr < N) {
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const u32x4 o = *reinterpret_cast<const u32x4*>(O + base + (int64_t)qr * D + 16 * ks + 8 * g);
-      const u32x4 d = bitcast<u32x4>(doB[ks]);
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const u32x4 o = orow[ks];
+    const u32x4 d = bitcast<u32x4>(doB[ks]);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        dpart = fmaf(bf16lo_to_f32(o[w]), bf16lo_to_f32(d[w]), dpart);
-        dpart = fmaf(bf16hi_to_f32(o[w]), bf16hi_to_f32(d[w]), dpart);
-      }
+    for (int w = 0; w < 4; ++w) {
+      dpart = fmaf(bf16lo_to_f32(o[w]), bf16lo_to_f32(d[w]), dpart);
+      dpart = fmaf(bf16hi_to_f32(o[w]), bf16hi_to_f32(d[w]), dpart);
     }
   }
   const float drow = dpart + shfl_xor_f32(dpart, 32);
-  const int64_t row = (int64_t)bh * N + qr;
-  const float nlse2 = qr < N ? -LSE[row] * kLog2e : kNegInf;
+  const float nlse2 = qr < N ? -lse * kLog2e : kNegInf;
   const u32x2 dwq = qr < N ? split3_bf16(-drow) : u32x2{0u, 0u};
   if (qr < N && g == 0) {
     delta[row] = drow;
@@ -882,12 +889,15 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     asm volatile("" : "+v"(sbf[0]), "+v"(sbf[1]));
   };
 
-  wait_copies(ntiles > 1);
+  // tile 0 before the first barrier; tiles 1 and 2 go out after the first
+  // products (a copy in flight there makes the compiler wait for every load)
+  wait_vm_at_most<0>();
   lds_barrier();
   if (!lead) lds_barrier();
-  if (ntiles > 2) issue_tile(2, sb2);
   read_rows(0, sb0);
   mph(0, sb0, false, true);
+  if (ntiles > 1) issue_tile(1, sb1);
+  if (ntiles > 2) issue_tile(2, sb2);
   lds_barrier();
   vph(0, true, 1, sb0);
   if (ntiles > 1) wait_copies(ntiles > 2);
