@@ -275,11 +275,14 @@ struct TileCopyBuf {
       dst[i] = 4 * c * 256;
     }
   }
+  // A tile that starts at or past nrows gets an empty descriptor: the copy
+  // reads no memory and fills the tile with zeros.
   __device__ __forceinline__ void issue(const __bf16* src, int nrows, int r0, unsigned char* tile) const {
-    const uint32_t bytes = (uint32_t)(nrows - r0) * (uint32_t)(D * 2);  // r0 < nrows
+    const int rb = min(r0, nrows);
+    const uint32_t bytes = (uint32_t)(nrows - rb) * (uint32_t)(D * 2);
 #pragma unroll
     for (int i = 0; i < kPerWave; ++i)
-      if (on[i]) buffer_to_lds16(src + (int64_t)r0 * D, bytes, voff[i], tile + dst[i]);
+      if (on[i]) buffer_to_lds16(src + (int64_t)rb * D, bytes, voff[i], tile + dst[i]);
   }
 };
 

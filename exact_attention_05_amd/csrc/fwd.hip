@@ -713,21 +713,23 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   lds_barrier();
   if (!lead) lds_barrier();
   mph(sb0, sb0, false, true);
-  if (ntiles > 1) issue_tile(1, sb1);
-  if (ntiles > 2) issue_tile(2, sb2);
-  if (ntiles > 3) issue_tile(3, sb3);
+  // tiles past the last are empty copies into ring slots no step reads, so
+  // the copies and the waits need no branches
+  issue_tile(1, sb1);
+  issue_tile(2, sb2);
+  issue_tile(3, sb3);
   // tile 1 (tiles 2 and 3 may still be in flight)
-  if (ntiles > 3) wait_vm_at_most<4>(); else if (ntiles > 2) wait_vm_at_most<2>(); else wait_vm_at_most<0>();
+  wait_vm_at_most<4>();
   lds_barrier();
   vph(0, sb0);
   // Tile j at cur, j-1 at prev; tile j+3 goes to far.
   auto step = [&](int j, const unsigned char* cur, const unsigned char* prev, unsigned char* far)
       __attribute__((always_inline)) {
     lds_barrier();
-    if (j + 3 < ntiles) issue_tile(j + 3, far);
+    issue_tile(j + 3, far);
     mph(cur, prev, true, true);
     // tile j+1 (tiles j+2 and j+3 may still be in flight)
-    if (j + 3 < ntiles) wait_vm_at_most<4>(); else if (j + 2 < ntiles) wait_vm_at_most<2>(); else wait_vm_at_most<0>();
+    wait_vm_at_most<4>();
     lds_barrier();
     vph(j, cur);
   };
@@ -738,6 +740,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     if (j + 3 < ntiles) step(j + 3, sb4, sb3, sb2);
     if (j + 4 < ntiles) step(j + 4, sb0, sb4, sb3);
   }
+  wait_vm_at_most<0>();  // the last (empty) copies land before the workgroup ends
   lds_barrier();
   {
     const int t = (ntiles - 1) % 5;
