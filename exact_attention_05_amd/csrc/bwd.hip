@@ -681,11 +681,13 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   if (!lead) lds_barrier();
   read_rows(0, sb0);
   mph(0, sb0, false, true);
-  if (ntiles > 1) issue_tile(i_begin + 1, sb1);
-  if (ntiles > 2) issue_tile(i_begin + 2, sb2);
+  // tiles past the last are empty copies into ring slots no step reads,
+  // so the copies and the waits need no branches
+  issue_tile(i_begin + 1, sb1);
+  issue_tile(i_begin + 2, sb2);
   lds_barrier();
   vph(i_begin * kT, true, 1, sb0);
-  if (ntiles > 1) wait_copies(ntiles > 2);
+  wait_copies(true);
   lds_barrier();
   mph(1, sb0, true, true);
   lds_barrier();
@@ -695,11 +697,11 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   auto step = [&](int s, const unsigned char* cur, const unsigned char* prev, const unsigned char* nxt1,
                   unsigned char* nxt2) __attribute__((always_inline)) {
     const int q0 = (i_begin + s) * kT;
-    if (s + 2 < ntiles) issue_tile(i_begin + s + 2, nxt2);
+    issue_tile(i_begin + s + 2, nxt2);
     mph(0, prev, true, true);
     lds_barrier();
     vph(q0, true, 1, cur);
-    if (s + 1 < ntiles) wait_copies(s + 2 < ntiles);
+    wait_copies(true);
     lds_barrier();
     mph(1, cur, true, true);
     lds_barrier();
@@ -719,6 +721,7 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     mph(0, last, true, false);
   }
   if (lead) lds_barrier();
+  wait_vm_at_most<0>();  // the last (empty) copies land before the workgroup ends
 
   if (key < N) {
     store_transposed_acc<D>(dV + base + (int64_t)key * D, dv, g, 1.f);
@@ -896,11 +899,13 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   if (!lead) lds_barrier();
   read_rows(0, sb0);
   mph(0, sb0, false, true);
-  if (ntiles > 1) issue_tile(1, sb1);
-  if (ntiles > 2) issue_tile(2, sb2);
+  // tiles past the last are empty copies into ring slots no step reads,
+  // so the copies and the waits need no branches
+  issue_tile(1, sb1);
+  issue_tile(2, sb2);
   lds_barrier();
   vph(0, true, 1, sb0);
-  if (ntiles > 1) wait_copies(ntiles > 2);
+  wait_copies(true);
   lds_barrier();
   mph(1, sb0, true, true);
   lds_barrier();
@@ -908,11 +913,11 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   lds_barrier();
   auto step = [&](int s, const unsigned char* cur, const unsigned char* prev, const unsigned char* nxt1,
                   unsigned char* nxt2) __attribute__((always_inline)) {
-    if (s + 2 < ntiles) issue_tile(s + 2, nxt2);
+    issue_tile(s + 2, nxt2);
     mph(0, prev, true, true);
     lds_barrier();
     vph(s * kT, true, 1, cur);
-    if (s + 1 < ntiles) wait_copies(s + 2 < ntiles);
+    wait_copies(true);
     lds_barrier();
     mph(1, cur, true, true);
     lds_barrier();
@@ -931,6 +936,7 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     mph(0, last, true, false);
   }
   if (lead) lds_barrier();
+  wait_vm_at_most<0>();  // the last (empty) copies land before the workgroup ends
 
   if (qr < N) store_transposed_acc<D>(dQ + base + (int64_t)qr * D, dq, g, scale);
 }
