@@ -29,7 +29,10 @@
 //     row order;
 //   * the causal mask is -inf on the diagonal tiles only; tiles above the
 //     diagonal are never loaded, and the longest query tiles are dispatched
-//     first (Triton tutorial, section 8.7.1).
+//     first (Triton tutorial, section 8.7.1).  d = 64: a wavefront stops
+//     computing after its last key tile with a visible key, and the two
+//     wavefronts of a SIMD own row blocks s and 7 - s of the query tile, so
+//     every SIMD has the same share of the diagonal.
 //   * attn_fwd_merge instantiates the same kernels with MERGE: the epilogue
 //     reads the row's running (O, LSE) and writes the result over both key
 //     sets (see merge_weights), so a Ring Attention step is one launch.
@@ -596,7 +599,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t base = (int64_t)bh * N * D;
   const int q0 = qtile * BR;
-  const int qw0 = q0 + wave * 32;
+  // the lead and the trail wavefront of SIMD s (w = s and w = s + 4) own row
+  // blocks s and 7 - s, so on a causal diagonal every SIMD has the same work
+  const int qw0 = q0 + 32 * (wave < 4 ? wave : 11 - wave);
   const int qr = qw0 + l32;
   const int kend = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kend + kBc - 1) / kBc;
@@ -733,19 +738,42 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     lds_barrier();
     vph(j, cur);
   };
-  for (int j = 1; j < ntiles; j += 5) {
+  // Causal: key tiles past the last one with a key visible to this
+  // wavefront's rows are masked out for all of them; the wavefront stops
+  // computing after that tile (nfull) and only copies and keeps the
+  // workgroup's barrier count in the remaining steps.
+  const int nfull = CAUSAL ? min(ntiles, (qw0 + 31) / kBc + 1) : ntiles;
+  for (int j = 1; j < nfull; j += 5) {
     step(j, sb1, sb0, sb4);
-    if (j + 1 < ntiles) step(j + 1, sb2, sb1, sb0);
-    if (j + 2 < ntiles) step(j + 2, sb3, sb2, sb1);
-    if (j + 3 < ntiles) step(j + 3, sb4, sb3, sb2);
-    if (j + 4 < ntiles) step(j + 4, sb0, sb4, sb3);
+    if (j + 1 < nfull) step(j + 1, sb2, sb1, sb0);
+    if (j + 2 < nfull) step(j + 2, sb3, sb2, sb1);
+    if (j + 3 < nfull) step(j + 3, sb4, sb3, sb2);
+    if (j + 4 < nfull) step(j + 4, sb0, sb4, sb3);
   }
-  wait_vm_at_most<0>();  // the last (empty) copies land before the workgroup ends
-  lds_barrier();
-  {
-    const int t = (ntiles - 1) % 5;
-    const unsigned char* last = t == 0 ? sb0 : t == 1 ? sb1 : t == 2 ? sb2 : t == 3 ? sb3 : sb4;
-    mph(last, last, true, false);
+  auto slot = [&](int t) __attribute__((always_inline)) -> unsigned char* {
+    t %= 5;
+    return t == 0 ? sb0 : t == 1 ? sb1 : t == 2 ? sb2 : t == 3 ? sb3 : sb4;
+  };
+  if (CAUSAL && nfull < ntiles) {
+    // the P~V product of tile nfull - 1 (its ring slot is overwritten only by
+    // tile nfull + 4, issued at the second step below)
+    lds_barrier();
+    issue_tile(nfull + 3, slot(nfull + 3));
+    mph(slot(nfull), slot(nfull - 1), true, false);
+    wait_vm_at_most<4>();
+    lds_barrier();
+    for (int j = nfull + 1; j < ntiles; ++j) {
+      lds_barrier();
+      issue_tile(j + 3, slot(j + 3));
+      wait_vm_at_most<4>();
+      lds_barrier();
+    }
+    wait_vm_at_most<0>();  // the last (empty) copies land before the workgroup ends
+    lds_barrier();
+  } else {
+    wait_vm_at_most<0>();  // the last (empty) copies land before the workgroup ends
+    lds_barrier();
+    mph(slot(ntiles - 1), slot(ntiles - 1), true, false);
   }
   if (lead) lds_barrier();
 
