@@ -10,7 +10,8 @@
 // (one K/V tile).  Eight wavefronts of 32 query rows per workgroup, two
 // workgroups per CU (four wavefronts per SIMD), the wavefronts of a workgroup
 // in two groups one phase apart as in the bf16 d = 64 kernel, 64-key tiles
-// copied HBM -> LDS ahead of use.
+// copied HBM -> LDS ahead of use; causal: as there, a wavefront stops after
+// its last key tile with a visible key and SIMD s holds row blocks s and 7 - s.
 // Per tile j and wavefront:
 //   S^T = K8 Q8^T     two FP8 MFMAs (keys 0-31, 32-63), the whole d = 64
 //                     reduction in one instruction each;
@@ -140,7 +141,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t base = (int64_t)bh * N * D;
   const int q0 = qtile * BR;
-  const int qw0 = q0 + wave * 32;
+  // the lead and the trail wavefront of SIMD s (w = s and w = s + 4) own row
+  // blocks s and 7 - s, so on a causal diagonal every SIMD has the same work
+  const int qw0 = q0 + 32 * (wave < NW / 2 ? wave : 3 * NW / 2 - 1 - wave);
   const int qr = qw0 + l32;
   const int kend = CAUSAL ? min(N, q0 + BR) : N;
   const int ntiles = (kend + kFp8Bc - 1) / kFp8Bc;
@@ -326,18 +329,44 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     lds_barrier();
     vph(j);
   };
-  for (int j = 1; j < ntiles; j += 5) {
+  // Causal: key tiles past the last one with a key visible to this
+  // wavefront's rows are masked out for all of them; the wavefront stops
+  // computing after that tile (nfull) and only copies and keeps the
+  // workgroup's barrier count in the remaining steps.
+  const int nfull = CAUSAL ? min(ntiles, (qw0 + 31) / kFp8Bc + 1) : ntiles;
+  for (int j = 1; j < nfull; j += 5) {
     step(j, sb1, sb0, sb4);
-    if (j + 1 < ntiles) step(j + 1, sb2, sb1, sb0);
-    if (j + 2 < ntiles) step(j + 2, sb3, sb2, sb1);
-    if (j + 3 < ntiles) step(j + 3, sb4, sb3, sb2);
-    if (j + 4 < ntiles) step(j + 4, sb0, sb4, sb3);
+    if (j + 1 < nfull) step(j + 1, sb2, sb1, sb0);
+    if (j + 2 < nfull) step(j + 2, sb3, sb2, sb1);
+    if (j + 3 < nfull) step(j + 3, sb4, sb3, sb2);
+    if (j + 4 < nfull) step(j + 4, sb0, sb4, sb3);
   }
-  lds_barrier();
-  {
-    const int t = (ntiles - 1) % 5;
-    const unsigned char* last = t == 0 ? sb0 : t == 1 ? sb1 : t == 2 ? sb2 : t == 3 ? sb3 : sb4;
-    mph(last, last, true, false, []() {});
+  auto slot = [&](int t) __attribute__((always_inline)) -> unsigned char* {
+    t %= 5;
+    return t == 0 ? sb0 : t == 1 ? sb1 : t == 2 ? sb2 : t == 3 ? sb3 : sb4;
+  };
+  if (CAUSAL && nfull < ntiles) {
+    // the P8 V product of tile nfull - 1 (its ring slot is overwritten only
+    // by tile nfull + 4, issued at the second step below)
+    {
+      const int j = nfull;
+      lds_barrier();
+      mph(slot(j), slot(j - 1), true, false, [&]() __attribute__((always_inline)) {
+        if (j + 3 < ntiles) issue_tile(j + 3, slot(j + 3));
+      });
+      if (j + 3 < ntiles) wait_vm_at_most<2>(); else if (j + 2 < ntiles) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
+      lds_barrier();
+    }
+    for (int j = nfull + 1; j < ntiles; ++j) {
+      lds_barrier();
+      if (j + 3 < ntiles) issue_tile(j + 3, slot(j + 3));
+      if (j + 3 < ntiles) wait_vm_at_most<2>(); else if (j + 2 < ntiles) wait_vm_at_most<1>(); else wait_vm_at_most<0>();
+      lds_barrier();
+    }
+    lds_barrier();
+  } else {
+    lds_barrier();
+    mph(slot(ntiles - 1), slot(ntiles - 1), true, false, []() {});
   }
   if (lead) lds_barrier();
 
