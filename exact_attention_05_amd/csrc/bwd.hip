@@ -15,6 +15,10 @@
 //                    S^T = K Q^T, dP^T = V dO^T, dS^T = P^T o (dP^T - D),
 //                    dQ^T += K^T dS^T.
 // dK and dQ are multiplied by the softmax scale at the end (section 8.8.4).
+// Causal, d = 64: a wavefront stops computing once the rest of its streamed
+// tiles are hidden from it (dK/dV visits query tiles last first for this),
+// and the two wavefronts of a SIMD own row blocks s and 7 - s, so every SIMD
+// has the same share of the diagonal.
 //
 // Variant with atomic dQ (the single-pass alternative that section 8.8
 // contrasts with the split into a dK/dV and a dQ kernel): bwd_dkdv also adds
@@ -542,7 +546,9 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t base = (int64_t)bh * N * D;
   const int k0 = ktile * BK;
-  const int kw0 = k0 + wave * 32;
+  // the lead and the trail wavefront of SIMD s (w = s and w = s + 4) own key
+  // blocks s and 7 - s, so on a causal diagonal every SIMD has the same work
+  const int kw0 = k0 + 32 * (wave < 4 ? wave : 11 - wave);
   const int key = kw0 + l32;
 
   const TileCopyBuf<D, NW> cp(wave, lane);
@@ -571,7 +577,14 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   };
 
   const int i_begin = CAUSAL ? k0 / kT : 0;
-  const int ntiles = (N + kT - 1) / kT - i_begin;
+  const int i_end = (N + kT - 1) / kT;
+  const int ntiles = i_end - i_begin;
+  // causal: query tiles are visited last first, so that on the diagonal the
+  // tiles hidden from a wavefront's keys come at the end of its sequence;
+  // positions past the sequence name the empty tile at i_end
+  auto tidx = [&](int s) __attribute__((always_inline)) {
+    return CAUSAL ? (s < ntiles ? i_end - 1 - s : i_end) : i_begin + s;
+  };
   // this wavefront's K and V rows first, then the first tile (loads
   // complete in issue order)
   bf16x8 kB[D / 16], vB[D / 16];
@@ -580,7 +593,7 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     kB[ks] = key < N ? *reinterpret_cast<const bf16x8*>(K + base + (int64_t)key * D + 16 * ks + 8 * g) : bf16x8{};
     vB[ks] = key < N ? *reinterpret_cast<const bf16x8*>(V + base + (int64_t)key * D + 16 * ks + 8 * g) : bf16x8{};
   }
-  issue_tile(i_begin, sb0);
+  issue_tile(tidx(0), sb0);
   const bf16x8 ones3 = bitcast<bf16x8>(g == 0 ? u32x4{0x3F803F80u, 0x3F80u, 0u, 0u} : u32x4{0u, 0u, 0u, 0u});
   f32x16 dk[D / 32], dv[D / 32];
 #pragma unroll
@@ -683,21 +696,21 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   mph(0, sb0, false, true);
   // tiles past the last are empty copies into ring slots no step reads,
   // so the copies and the waits need no branches
-  issue_tile(i_begin + 1, sb1);
-  issue_tile(i_begin + 2, sb2);
+  issue_tile(tidx(1), sb1);
+  issue_tile(tidx(2), sb2);
   lds_barrier();
-  vph(i_begin * kT, true, 1, sb0);
+  vph(tidx(0) * kT, true, 1, sb0);
   wait_copies(true);
   lds_barrier();
   mph(1, sb0, true, true);
   lds_barrier();
-  vph(i_begin * kT + 32, ntiles > 1, 0, sb1);
+  vph(tidx(0) * kT + 32, ntiles > 1, 0, sb1);
   lds_barrier();
   // Tile s >= 1 at cur, s-1 at prev, s+1 at nxt1; tile s+2 goes to nxt2.
   auto step = [&](int s, const unsigned char* cur, const unsigned char* prev, const unsigned char* nxt1,
                   unsigned char* nxt2) __attribute__((always_inline)) {
-    const int q0 = (i_begin + s) * kT;
-    issue_tile(i_begin + s + 2, nxt2);
+    const int q0 = tidx(s) * kT;
+    issue_tile(tidx(s + 2), nxt2);
     mph(0, prev, true, true);
     lds_barrier();
     vph(q0, true, 1, cur);
@@ -708,17 +721,35 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     vph(q0 + 32, s + 1 < ntiles, 0, nxt1);
     lds_barrier();
   };
-  for (int s = 1; s < ntiles; s += 4) {
+  // Causal: query tiles before the first one with a query that sees this
+  // wavefront's keys (the last ones visited) are masked out for all of
+  // them; the wavefront stops computing after the first (nfull) and only
+  // copies and keeps the workgroup's barrier count in the remaining steps.
+  const int nfull = CAUSAL ? max(1, min(ntiles, i_end - kw0 / kT)) : ntiles;
+  for (int s = 1; s < nfull; s += 4) {
     step(s, sb1, sb0, sb2, sb3);
-    if (s + 1 < ntiles) step(s + 1, sb2, sb1, sb3, sb0);
-    if (s + 2 < ntiles) step(s + 2, sb3, sb2, sb0, sb1);
-    if (s + 3 < ntiles) step(s + 3, sb0, sb3, sb1, sb2);
+    if (s + 1 < nfull) step(s + 1, sb2, sb1, sb3, sb0);
+    if (s + 2 < nfull) step(s + 2, sb3, sb2, sb0, sb1);
+    if (s + 3 < nfull) step(s + 3, sb0, sb3, sb1, sb2);
   }
-  // Contraction of the last half.
-  {
-    const int t = (ntiles - 1) & 3;
-    const unsigned char* last = t == 0 ? sb0 : t == 1 ? sb1 : t == 2 ? sb2 : sb3;
-    mph(0, last, true, false);
+  auto slot = [&](int t) __attribute__((always_inline)) -> unsigned char* {
+    t &= 3;
+    return t == 0 ? sb0 : t == 1 ? sb1 : t == 2 ? sb2 : sb3;
+  };
+  // contraction of the last half of tile position nfull - 1 (its ring slot is
+  // overwritten only by position nfull + 3, issued at the second step below)
+  if (CAUSAL && nfull < ntiles) {
+    for (int s = nfull; s < ntiles; ++s) {
+      issue_tile(tidx(s + 2), slot(s + 2));
+      if (s == nfull) mph(0, slot(nfull - 1), true, false);
+      lds_barrier();
+      wait_copies(true);
+      lds_barrier();
+      lds_barrier();
+      lds_barrier();
+    }
+  } else {
+    mph(0, slot(ntiles - 1), true, false);
   }
   if (lead) lds_barrier();
   wait_vm_at_most<0>();  // the last (empty) copies land before the workgroup ends
@@ -758,7 +789,9 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t base = (int64_t)bh * N * D;
   const int q0 = qtile * BQ;
-  const int qw0 = q0 + wave * 32;
+  // the lead and the trail wavefront of SIMD s (w = s and w = s + 4) own row
+  // blocks s and 7 - s, so on a causal diagonal every SIMD has the same work
+  const int qw0 = q0 + 32 * (wave < 4 ? wave : 11 - wave);
   const int qr = qw0 + l32;
 
   const TileCopyBuf<D, NW> cp(wave, lane);
@@ -924,16 +957,35 @@ __global__ __launch_bounds__(kPPThreads) __attribute__((amdgpu_waves_per_eu(2, 2
     vph(s * kT + 32, s + 1 < ntiles, 0, nxt1);
     lds_barrier();
   };
-  for (int s = 1; s < ntiles; s += 4) {
+  // Causal: key tiles past the last one with a key visible to this
+  // wavefront's rows are masked out for all of them; the wavefront stops
+  // computing after that tile (nfull) and only copies and keeps the
+  // workgroup's barrier count in the remaining steps.
+  const int nfull = CAUSAL ? min(ntiles, (qw0 + 31) / kT + 1) : ntiles;
+  for (int s = 1; s < nfull; s += 4) {
     step(s, sb1, sb0, sb2, sb3);
-    if (s + 1 < ntiles) step(s + 1, sb2, sb1, sb3, sb0);
-    if (s + 2 < ntiles) step(s + 2, sb3, sb2, sb0, sb1);
-    if (s + 3 < ntiles) step(s + 3, sb0, sb3, sb1, sb2);
+    if (s + 1 < nfull) step(s + 1, sb2, sb1, sb3, sb0);
+    if (s + 2 < nfull) step(s + 2, sb3, sb2, sb0, sb1);
+    if (s + 3 < nfull) step(s + 3, sb0, sb3, sb1, sb2);
   }
-  {
-    const int t = (ntiles - 1) & 3;
-    const unsigned char* last = t == 0 ? sb0 : t == 1 ? sb1 : t == 2 ? sb2 : sb3;
-    mph(0, last, true, false);
+  auto slot = [&](int t) __attribute__((always_inline)) -> unsigned char* {
+    t &= 3;
+    return t == 0 ? sb0 : t == 1 ? sb1 : t == 2 ? sb2 : sb3;
+  };
+  // contraction of the last half of tile nfull - 1 (its ring slot is
+  // overwritten only by tile nfull + 3, issued at the second step below)
+  if (CAUSAL && nfull < ntiles) {
+    for (int s = nfull; s < ntiles; ++s) {
+      issue_tile(s + 2, slot(s + 2));
+      if (s == nfull) mph(0, slot(nfull - 1), true, false);
+      lds_barrier();
+      wait_copies(true);
+      lds_barrier();
+      lds_barrier();
+      lds_barrier();
+    }
+  } else {
+    mph(0, slot(ntiles - 1), true, false);
   }
   if (lead) lds_barrier();
   wait_vm_at_most<0>();  // the last (empty) copies land before the workgroup ends
