@@ -264,7 +264,7 @@ def main():
     if a.fwd_seq:
         FWD["N"] = a.fwd_seq
     if a.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(the per-(b, h) work would shard over GPUs with no communication).", file=sys.stderr)
         sys.exit(2)
 
