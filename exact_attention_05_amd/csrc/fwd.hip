@@ -120,7 +120,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   if (CAUSAL) qtile = n_qtiles - 1 - qtile;  // longest rows first
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t base = (int64_t)bh * N * D;
   const __bf16* Qh = Q + base;
@@ -425,7 +425,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(
   if (CAUSAL) qtile = n_qtiles - 1 - qtile;
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, l32 = lane & 31;
   const int64_t base = (int64_t)bh * N * D;
   const float* Qh = Q + base;
