@@ -233,8 +233,10 @@ def cpu_baseline_others(budget_s=3.0, max_decode_heads=16):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    # 50 steps of about 6 ms: the means below are over enough launches that one
+    # slow launch (seen now and then on a fresh device) moves them little
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-long", action="store_true", help="skip the reported-only long causal forward")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
