@@ -248,17 +248,19 @@ def test_fp8_pipeline_from_bf16():
     _assert_fp8("fp8 pipeline", o, lse, O, LSE, A)
 
 
-def test_fp8_fwd_workload_sampled():
-    """E4M3 Q, K, V [4, 16, 2048, 64] (grid codes) with block scales, non-causal,
-    scale 1/8: sampled heads against the oracle."""
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_fwd_workload_sampled(causal):
+    """E4M3 Q, K, V [4, 16, 2048, 64] (grid codes) with block scales, scale
+    1/8: sampled heads against the oracle (causal: the launch fills the chip
+    at once, so the long/short pairing and the per-wavefront stop run)."""
     B, H, N = 4, 16, 2048
-    _say(f"fp8 fwd workload [{B},{H},{N},64]")
+    _say(f"fp8 fwd workload [{B},{H},{N},64] causal={causal}")
     ins = _fp8_inputs(0, B, H, N)
-    o, lse = _run_fp8(*ins, 0.125, False)
+    o, lse = _run_fp8(*ins, 0.125, causal)
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
     for b, h in ((0, 0), (3, 15)):
         sub = [t[b:b + 1, h:h + 1] for t in ins]
-        _assert_fp8(f"fp8[{b},{h}]", o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], *_oracle(*sub, 0.125, False))
+        _assert_fp8(f"fp8[{b},{h}]", o[b:b + 1, h:h + 1], lse[b:b + 1, h:h + 1], *_oracle(*sub, 0.125, causal))
 
 
 def test_fp8_fwd_offsets_beyond_2gib():
