@@ -27,7 +27,11 @@
 //                     its own scales; the listing scales the whole accumulator)
 //                     before the next tile's score products, so T and S are
 //                     never live together (no register spills at 128 VGPRs)
-// and at the end O = U / l, LSE = (m + log2 l) ln 2.  Rows past N do not take
+// and at the end O = U / l, LSE = (m + log2 l) ln 2.  The kernel keeps U and l
+// multiplied by 2^(m - mref), mref a per-row reference (the first visible
+// block's m, moved up when m passes it by 64): alpha U then needs no
+// multiply, a block's T goes in with the factor scale_p sv_j 2^(m_new - mref),
+// the factor cancels in O, and LSE = (mref + log2 l) ln 2.  Rows past N do not take
 // part in the block's max.  P8 goes from the score accumulator straight into
 // the B operand (a lane holds 32 keys of its query); the V^T operand is read
 // with transposing 8-bit LDS reads whose source rows follow the same key
@@ -189,8 +193,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
 
   f32x16 oacc[2] = {f32x16{}, f32x16{}};
   f32x16 tacc[2];  // T = V8^T P8^T of the previous tile
-  float m = kNegInf, lsum = 0.f;
-  float alpha_prev = 1.f, f_prev = 0.f;  // the previous tile's alpha (per row) and scale_p sv (per wavefront)
+  // U and l are kept multiplied by 2^(m - mref): a block's product then goes
+  // in with one fma, and the factor cancels in O = U / l (LSE = mref + log2 l)
+  float m = kNegInf, mref = kNegInf, lsum = 0.f;
+  float f_prev = 0.f;  // the previous tile's scale_p sv 2^(m - mref) (per row)
   f32x16 sacc[2];
   i32x8 pb = {};  // P8 of the current tile, the B operand of T
   float ck = cq * ksh[0];
@@ -216,12 +222,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
       va[mt] = i32x8{r[0][0], r[0][1], r[1][0], r[1][1], r[2][0], r[2][1], r[3][0], r[3][1]};
     }
   };
-  // U = alpha U + f T for the previous tile's product
+  // U += f T for the previous tile's product (f carries the frame factor)
   auto accumulate = [&]() __attribute__((always_inline)) {
-    if (__builtin_expect(__ballot(alpha_prev != 1.f) != 0, 0)) {
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) oacc[mt] *= alpha_prev;
-    }
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -280,7 +282,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     const float mx = max_of_halves(vmax(mx0, mx1));
     const float bm = mx * ck;  // the row's largest u in this block (-inf: none visible)
     const float m_new = vmax(m, bm);
-    const float alpha = m_new == kNegInf ? 1.f : fast_exp2(m - m_new);
+    // the first visible block fixes the frame; a frame more than 2^64 below
+    // the running max is moved up to it (rare: U and l are rescaled)
+    if (__builtin_expect(__ballot(m_new - mref > 64.f) != 0, 0)) {
+      const float r = m_new - mref > 64.f ? fast_exp2(mref - m_new) : 1.f;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) oacc[mt] *= r;
+      lsum *= r;
+      mref = m_new - mref > 64.f ? m_new : mref;
+    }
+    mref = mref == kNegInf ? m_new : mref;
+    const float gf = m_new == kNegInf ? 0.f : fast_exp2(m_new - mref);
     // e = log2 of the block's largest p, over its rows below N
     const float e = max_over_32_lanes(qr < N ? bm - m_new : kNegInf);
     const float off = e == kNegInf ? 0.f : m_new + e - kLog2P8Max;
@@ -299,10 +311,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
     }
     const float rs = (r4[0] + r4[1]) + (r4[2] + r4[3]);
     const float sp = fast_exp2(e) * (1.f / kP8Max);  // scale_p (0 for an empty block)
-    lsum = fmaf(rs, sp, lsum * alpha);
+    lsum = fmaf(rs, sp * gf, lsum);
     m = m_new;
-    alpha_prev = alpha;
-    f_prev = sp * vsh[j];
+    f_prev = sp * vsh[j] * gf;
     if (j + 1 < ntiles) ck = cq * ksh[j + 1];
     asm volatile("" : "+v"(pb));
   };
@@ -383,7 +394,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
                    pack_bf16x2(oacc[mt][4 * c + 2] * inv, oacc[mt][4 * c + 3] * inv)};
         *reinterpret_cast<u32x2*>(Oh + (int64_t)qr * D + d0) = w;
       }
-    if (g == 0 && LSE != nullptr) LSE[(int64_t)bh * N + qr] = lt > 0.f ? (m + fast_log2(lt)) * kLn2 : kNegInf;
+    if (g == 0 && LSE != nullptr) LSE[(int64_t)bh * N + qr] = lt > 0.f ? (mref + fast_log2(lt)) * kLn2 : kNegInf;
   }
 }
 
