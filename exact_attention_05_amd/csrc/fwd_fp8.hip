@@ -231,7 +231,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   };
 
   // M: T = V^T P8^T of the previous tile, added into U with that tile's
-  // alpha and scales, then S^T of this one; the K operands are read after the
+  // factor, then S^T of this one; the K operands are read after the
   // addition so that T and S are never live together.  `copy` runs after the
   // V operand reads: a tile copy issued before them makes the compiler wait
   // for it (it cannot always tell the buffers apart).
