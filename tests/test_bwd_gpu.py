@@ -74,6 +74,30 @@ def test_bwd_ragged(N, d, causal):
     assert np.all(lparts[:, 3] == 0)
 
 
+@pytest.mark.parametrize("d,scale", [(64, 0.3), (64, 0.02), (128, 0.05), (128, 0.3)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_other_scales(d, scale, causal):
+    """Softmax scales other than 1/sqrt(d) (the scale enters the exponent, the
+    -LSE split and the final scaling of dK and dQ): every gradient against
+    the oracle at N = 300 (two key workgroups, ragged).  Q and K are drawn
+    with standard deviation (scale sqrt(d))^(-1/2), so the scaled scores
+    spread as at the default scale and the gradients keep the magnitudes at
+    which the absolute bf16 bar applies (P and dS enter the gradient products
+    in bf16, so the error grows with the gradients)."""
+    N = 300
+    _say(f"bwd d={d} scale={scale} causal={causal}")
+    seed = N + d + 7
+    sd = (scale * math.sqrt(d)) ** -0.5
+    q, k = (make_tensor(seed, n, 1, 2, N, d, torch.bfloat16, sd) for n in ("q", "k"))
+    v, dO = (make_tensor(seed, n, 1, 2, N, d, torch.bfloat16) for n in ("v", "do"))
+    dq, dk, dv, _, _ = _gpu_bwd(q, k, v, dO, scale, causal)
+    Q, K, V, DO = (widen(t) for t in (q, k, v, dO))
+    dQ, dK, dV = ref_bwd(Q, K, V, DO, scale, causal)
+    assert_bar("dV", widen(dv), dV, torch.bfloat16)
+    assert_bar("dK", widen(dk), dK, torch.bfloat16)
+    assert_bar("dQ", widen(dq), dQ, torch.bfloat16)
+
+
 def test_bwd_invariants():
     """sum_j dK_j = 0 (rows of dS sum to zero); Q = 0 gives dK = 0."""
     _say("bwd invariants")

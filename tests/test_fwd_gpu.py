@@ -67,6 +67,20 @@ def test_bf16_ragged(N, d, causal):
     assert_lse("LSE", lse, LSE)
 
 
+@pytest.mark.parametrize("d,scale", [(64, 0.3), (64, 0.02), (128, 0.05), (128, 0.4)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bf16_other_scales(d, scale, causal):
+    """Softmax scales other than 1/sqrt(d) (folded into the exponent's base-2
+    factor): O and LSE against the oracle at N = 300."""
+    N = 300
+    _say(f"bf16 d={d} scale={scale} causal={causal}")
+    q, k, v = _inputs(N + 3 * d, 2, 3, N, d, torch.bfloat16)
+    o, lse = _run(q, k, v, scale, causal)
+    O, LSE = ref_fwd(widen(q), widen(k), widen(v), scale, causal)
+    assert_bar("O", o, O, torch.bfloat16)
+    assert_lse("LSE", lse, LSE)
+
+
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("N", [1, 31, 256, 300])
 def test_f32(N, causal):
