@@ -61,6 +61,25 @@ def test_bwd_atomic_ragged(B, H, N, d, causal):
         assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
 
+@pytest.mark.parametrize("d,scale", [(64, 0.3), (128, 0.05)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_bwd_atomic_other_scales(d, scale, causal):
+    """A softmax scale other than 1/sqrt(d) (it enters the exponent, the -LSE
+    split and the final scaling of dK and of the accumulated dQ), with Q and
+    K drawn so that the scaled scores spread as at the default scale."""
+    N = 300
+    _say(f"bwd atomic d={d} scale={scale} causal={causal}")
+    seed = 700 + d
+    sd = (scale * math.sqrt(d)) ** -0.5
+    q, k = (make_tensor(seed, n, 1, 2, N, d, torch.bfloat16, sd, device=DEV) for n in ("q", "k"))
+    v, dO = (make_tensor(seed, n, 1, 2, N, d, torch.bfloat16, device=DEV) for n in ("v", "do"))
+    (dq, dk, dv, _), _ = _both(q, k, v, dO, scale, causal)
+    dQ, dK, dV = ref_bwd(*(widen(t.cpu()) for t in (q, k, v, dO)), scale, causal)
+    assert_bar("dQ", widen(dq), dQ, torch.bfloat16)
+    assert_bar("dK", widen(dk), dK, torch.bfloat16)
+    assert_bar("dV", widen(dv), dV, torch.bfloat16)
+
+
 def test_bwd_atomic_repeats():
     """dK and dV repeat bit for bit; dQ to the bar."""
     _say("bwd atomic repeat")
