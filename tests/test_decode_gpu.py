@@ -60,6 +60,24 @@ def test_decode_small(L, S, d):
     _check_partials(ws, B, H, d, S, qq, kk, vv, scale)
 
 
+@pytest.mark.parametrize("d,scale", [(64, 0.3), (64, 0.02), (128, 0.4), (128, 0.05)])
+def test_decode_other_scales(d, scale):
+    """Softmax scales other than 1/sqrt(d): O, LSE and the chunk partials
+    against the oracle."""
+    L, S, B, H = 1000, 7, 2, 3
+    _say(f"decode d={d} scale={scale}")
+    q = make_tensor(L + d, "q", B, H, 1, d, torch.bfloat16)
+    k = make_tensor(L + d, "k", B, H, L, d, torch.bfloat16)
+    v = make_tensor(L + d, "v", B, H, L, d, torch.bfloat16)
+    o, lse, ws = attn_fwd_splitk_decode(q.to(DEV), k.to(DEV), v.to(DEV), S, scale=scale)
+    torch.cuda.synchronize()
+    qq, kk, vv = widen(q), widen(k), widen(v)
+    O, LSE = ref_fwd(qq, kk, vv, scale, False)
+    assert_bar("O", widen(o), O, torch.bfloat16)
+    assert_lse("LSE", widen(lse), LSE[..., 0])
+    _check_partials(ws, B, H, d, S, qq, kk, vv, scale)
+
+
 @pytest.mark.parametrize("B,H,L,S", [(2, 32, 40000, 256), (4, 16, 100, 256), (4, 16, 3001, 128)])
 def test_decode_large_grids(B, H, L, S):
     """Grids of 8192 chunks and more: long chunks (156 keys), mostly empty

@@ -179,6 +179,18 @@ def test_fp8_fwd_ragged(N, causal):
     _assert_fp8("fp8", o, lse, *_oracle(*ins, 0.125, causal))
 
 
+@pytest.mark.parametrize("scale", [0.3, 0.05])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_fwd_other_scales(scale, causal):
+    """Softmax scales other than 1/8 (the scale multiplies the block scales'
+    product in every score): against the oracle at N = 300."""
+    N = 300
+    _say(f"fp8 fwd scale={scale} causal={causal}")
+    ins = _fp8_inputs(N + 64, 1, 2, N)
+    o, lse = _run_fp8(*ins, scale, causal)
+    _assert_fp8("fp8", o, lse, *_oracle(*ins, scale, causal))
+
+
 @pytest.mark.parametrize("causal", [False, True])
 def test_fp8_fwd_general_codes(causal):
     """Codes over the whole E4M3 range (scores not exact in the matrix
