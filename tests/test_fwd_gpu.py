@@ -192,19 +192,21 @@ def test_batched_noncausal_workload_sampled():
         assert_lse(f"LSE[{b},{h}]", widen(lse[b, h]), LSE)
 
 
-def test_batched_causal_workload_full_heads():
-    """bf16 [B=4, H=16, N=2048, d=64], iid N(0, 1), causal: the launch fills
-    the chip at once (512 workgroups), so long and short query tiles are
-    paired per CU and every wavefront stops after its last visible key tile;
-    every row of 4 heads against the oracle."""
-    B, H, N, d = 4, 16, 2048, 64
+@pytest.mark.parametrize("B,H,N,heads", [(4, 16, 2048, ((0, 0), (1, 9), (2, 4), (3, 15))),
+                                          (2, 16, 4096, ((0, 0), (1, 15)))])
+def test_batched_causal_workload_full_heads(B, H, N, heads):
+    """bf16 [B, H, N, d=64], iid N(0, 1), causal, 512 workgroups (8 or 16
+    query tiles per head): the launch fills the chip at once, so long and
+    short query tiles are paired per CU and every wavefront stops after its
+    last visible key tile; every row of the sampled heads against the oracle."""
+    d = 64
     _say(f"workload [{B},{H},{N},{d}] causal")
     seed = 3
     q, k, v = (make_tensor(seed, n, B, H, N, d, torch.bfloat16, device=DEV) for n in ("q", "k", "v"))
     o, lse = attn_fwd(q, k, v, scale=1.0 / math.sqrt(d), causal=True)
     torch.cuda.synchronize()
     assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
-    for b, h in ((0, 0), (1, 9), (2, 4), (3, 15)):
+    for b, h in heads:
         qh, kh, vh = (widen(make_head(seed, n, b, h, N, d, torch.bfloat16)) for n in ("q", "k", "v"))
         O, LSE = ref_fwd(qh, kh, vh, 1.0 / math.sqrt(d), True)
         assert_bar(f"O[{b},{h}]", widen(o[b, h]), O, torch.bfloat16)
