@@ -318,7 +318,8 @@ def cmd_cycles(a):
         lines += ["", f"Per tile and wavefront (from {la} and {lb}): {inc['SQ_INSTS_VALU']:.1f} VALU instructions, of "
                   f"which {inc['SQ_INSTS_MFMA']:.1f} MFMA (SQ_INSTS_VALU counts them) and "
                   f"{inc['SQ_INSTS_VALU_TRANS_F32']:.1f} transcendental, so "
-                  f"{inc['SQ_INSTS_VALU'] - inc['SQ_INSTS_MFMA']:.1f} other vector instructions; "
+                  f"{inc['SQ_INSTS_VALU'] - inc['SQ_INSTS_MFMA'] - inc['SQ_INSTS_VALU_TRANS_F32']:.1f} "
+                  f"other vector instructions; "
                   f"{inc['SQ_INSTS_SALU']:.1f} scalar. Per wavefront outside the loop: {fixed:.0f} VALU instructions."]
     text = "\n".join(lines) + "\n"
     if a.out:
