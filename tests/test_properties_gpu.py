@@ -10,8 +10,9 @@ every element (no oracle needed):
 * the softmax weights of a row sum to one: V = 1 gives O = 1.
 
 The launches are the bench configurations: the forward [4,16,2048,64] in
-both mask settings and [2,32,8192,128] causal, the split-K decode
-[16,32,32768,128] over 256 chunks and the causal backward [2,16,4096,64].
+both mask settings (bf16 and FP8) and [2,32,8192,128] causal, the split-K
+decode [16,32,32768,128] over 256 chunks and the backward [2,16,4096,64]
+(causal, and non-causal for the key permutation).
 """
 
 import sys
@@ -20,7 +21,7 @@ import numpy as np
 import pytest
 import torch
 
-from exact_attention_05_amd import attn_bwd, attn_fwd, attn_fwd_splitk_decode
+from exact_attention_05_amd import attn_bwd, attn_fwd, attn_fwd_fp8, attn_fwd_splitk_decode, attn_quantize_fp8
 from exact_attention_05_amd.inputs import make_tensor, widen
 
 from helpers import assert_bar, assert_lse
@@ -132,3 +133,50 @@ def test_bwd_heads_independent():
     torch.cuda.synchronize()
     for name, a, b in (("dQ", dqp, dq), ("dK", dkp, dk), ("dV", dvp, dv)):
         assert torch.equal(a.reshape(B * H, N, d), b.reshape(B * H, N, d)[perm]), name
+
+
+def test_bwd_key_permutation_noncausal():
+    """Non-causal backward [2,16,4096,64]: with the keys and values reversed
+    within every head, dK and dV come out reversed and dQ unchanged, up to
+    rounding (the gradients of a weighted mean over the key set)."""
+    B, H, N, d = 2, 16, 4096, 64
+    _say(f"bwd key permutation [{B},{H},{N},{d}]")
+    q, k, v = _qkv(52, B, H, N, d)
+    do = make_tensor(52, "do", B, H, N, d, torch.bfloat16, device=DEV)
+    o, lse = attn_fwd(q, k, v, causal=False)
+    dq, dk, dv, ws = attn_bwd(q, k, v, o, do, lse, causal=False)
+    idx = torch.arange(N - 1, -1, -1, device=DEV)
+    kr, vr = k[:, :, idx].contiguous(), v[:, :, idx].contiguous()
+    orv, lser = attn_fwd(q, kr, vr, causal=False)
+    dqr, dkr, dvr, _ = attn_bwd(q, kr, vr, orv, do, lser, causal=False, workspace=ws)
+    torch.cuda.synchronize()
+    assert_bar("dQ", widen(dqr), widen(dq), torch.bfloat16)
+    assert_bar("dK", widen(dkr[:, :, idx]), widen(dk), torch.bfloat16)
+    assert_bar("dV", widen(dvr[:, :, idx]), widen(dv), torch.bfloat16)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_heads_independent(causal):
+    """FP8 [4,16,2048,64]: quantising and running the permuted heads gives
+    the permuted codes, scales and outputs bitwise."""
+    B, H, N, d = 4, 16, 2048, 64
+    _say(f"fp8 head permutation [{B},{H},{N},{d}] causal={causal}")
+    q, k, v = _qkv(53, B, H, N, d)
+
+    def run(q, k, v):
+        q8, sq = attn_quantize_fp8(q, 32)
+        k8, sk = attn_quantize_fp8(k, 64)
+        v8, sv = attn_quantize_fp8(v, 64)
+        o, lse = attn_fwd_fp8(q8, k8, v8, sq, sk, sv, causal=causal)
+        return q8, sq, o, lse
+
+    q8, sq, o, lse = run(q, k, v)
+    qp, perm = _permute_heads(q, B, H)
+    kp, _ = _permute_heads(k, B, H)
+    vp, _ = _permute_heads(v, B, H)
+    q8p, sqp, op, lsep = run(qp, kp, vp)
+    torch.cuda.synchronize()
+    assert torch.equal(q8p.reshape(B * H, -1), q8.reshape(B * H, -1)[perm])
+    assert torch.equal(sqp.reshape(B * H, -1), sq.reshape(B * H, -1)[perm])
+    assert torch.equal(op.reshape(B * H, N, d), o.reshape(B * H, N, d)[perm])
+    assert torch.equal(lsep.reshape(B * H, N), lse.reshape(B * H, N)[perm])
